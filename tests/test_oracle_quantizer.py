@@ -136,6 +136,15 @@ def test_constant_and_on_grid_groups_are_exact():
     assert np.array_equal(deq2[1], K[1].astype(np.float64))
 
 
+def test_signed_zero_minimum_is_stored_as_plus_zero():
+    x = np.zeros((1, 128), np.float16)
+    x[0, 5] = np.float16(-0.0)
+    x[0, 40:72] = np.float16(-0.0)
+    pk = orc.quantize_k(x)
+    assert (pk["zero"].view(np.uint16) == 0).all()
+    assert (pk["scale"].view(np.uint16) == 0).all() and (pk["rscale"].view(np.uint16) == 0).all()
+
+
 def test_tiny_residual_below_rscale_resolution_is_dropped():
     """A residual too small for a nonzero fp16 rscale leaves res = 0 (rscale = 0)."""
     x = np.zeros(32)
