@@ -20,7 +20,8 @@ Readings where the page leaves a step open (each is listed with its reason
 in the design notes of the repository):
 
 * The page does not define the quantizer.  Per token and per 32-channel
-  group: zero = group min (+0 when that min is a signed zero); scale = fp16(RNE((max - min) / 3)); 2-bit code
+  group: zero = group min; scale = fp16(RNE((max - min) / 3)); a signed
+  zero in either is stored as +0; 2-bit code
   = number of k in {1,2,3} with x - zero >= (k - 1/2) scale (0 when scale
   is 0); residual r = x - (zero + code * scale); residual scale =
   fp16(RNE(max|r| / 127)); int8 residual = sign(r) * min(127, number of
@@ -76,7 +77,7 @@ def quantize_k(K16: np.ndarray) -> Dict[str, np.ndarray]:
     x = K16.astype(np.float64).reshape(lead + (N_GROUPS, GROUP))
 
     zero = x.min(axis=-1) + 0.0          # a signed-zero minimum is stored as +0
-    scale = f16_round((x.max(axis=-1) - zero) / 3.0)
+    scale = f16_round((x.max(axis=-1) - zero) / 3.0) + 0.0
     d = x - zero[..., None]
     s = scale[..., None]
     # count of thresholds (k - 1/2) * scale, k = 1..3, that x - zero reaches
