@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark one FFD decode-attention step on one MI355X; prints one JSON line.
+
+A step is the whole hot path for one layer: pseudo-max, fused Top-delta scan +
+refine, log-sum-exp merge (three kernel launches), over inputs already resident
+in HBM.  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
+delta=5), plus the 256K long-context shape with the in-house dense
+flash-decode kernel timed beside it.
+
+Timing: W untimed warm-up steps, then exactly K timed steps bracketed by
+torch.cuda.synchronize(); per-layer caches are rotated (each step reads a
+different copy) so that the bytes touched between two visits of the same copy
+exceed the 256 MB last-level cache.  The fused scan + refine kernel is also
+timed per launch with HIP events recorded by the library on the launch stream.
+
+Roofline: achieved = algorithmic bytes of the fused kernel per launch (48 B per
+token-head scanned + 392 B per kept token-head refined) / its mean duration,
+against the 8 TB/s HBM3E peak.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+SCAN_BYTES = 48      # 2-bit codes 32 B + (scale, zero) 16 B per token-head
+REFINE_BYTES = 392   # int8 residual 128 B + rscale 8 B + fp16 V 256 B per kept token-head
+PSEUDO_BYTES = 184   # packed K (codes, scale/zero, residual, rscale) per support token-head
+DENSE_BYTES = 512    # fp16 K + V per token-head
+ROTATE_TARGET = 1.5e9
+METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
+
+
+class HipEvents:
+    """Minimal hipEvent API through ctypes (events recorded by libffd itself)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        assert self.h.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, e: int) -> None:
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def prepare(w, seed, torch):
+    from synthetic import make_case
+    t0 = time.time()
+    c = make_case(w, seed)
+    log(f"generated {w.name} in {time.time() - t0:.1f}s")
+    return c, {k: to_dev(v, torch) for k, v in c.items()}
+
+
+def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
+    base = ffd.PackedCache(shape, v=d["v"])
+    ffd.quantize_k(shape, d["k"], 0, w.max_len, base)
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+    nb = w.max_len // 64
+    keep = torch.zeros((w.batch, w.kv_heads, nb), dtype=torch.uint8, device="cuda")
+    ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, out, ws, debug={"keep": keep})
+    torch.cuda.synchronize()
+    keep = keep.cpu().numpy().astype(bool)
+    lens = c["seq_lens"].astype(np.int64)
+    tok_total = int(lens.sum()) * w.kv_heads
+    kept_tok = 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        nbb = (L + 63) // 64
+        per_tok = np.repeat(keep[b, :, :nbb], 64, axis=1)[:, :L]
+        kept_tok += int(per_tok.sum())
+    keep_frac = kept_tok / tok_total
+    attend_bytes = SCAN_BYTES * tok_total + REFINE_BYTES * kept_tok
+    support = sum(min(int(L), w.sink + w.local) for L in lens) * w.kv_heads
+    step_bytes = attend_bytes + PSEUDO_BYTES * support
+
+    layer_bytes = sum(getattr(base, f).numel() for f in ("codes", "sz", "res", "rscale")) + d["v"].numel() * 2
+    R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
+    layers = [base]
+    for _ in range(R - 1):
+        cc = ffd.PackedCache.__new__(ffd.PackedCache)
+        cc.shape = shape
+        for f in ("codes", "sz", "res", "rscale"):
+            setattr(cc, f, getattr(base, f).clone())
+        cc.v = d["v"].clone()
+        layers.append(cc)
+    log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
+
+    ev = HipEvents()
+    evs = [(ev.create(), ev.create()) for _ in range(steps)]
+    for i in range(warmup):
+        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        a, b = evs[i]
+        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
+                        debug={"attend_start": a, "attend_stop": b})
+    t_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_stop)
+    attend_ms = [ev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        ev.destroy(a)
+        ev.destroy(b)
+    us_step = total_ms * 1e3 / steps
+    attend_us = statistics.mean(attend_ms) * 1e3
+    return {
+        "us_per_step": us_step,
+        "wall_us_per_step": wall * 1e6 / steps,
+        "attend_us_mean": attend_us,
+        "attend_us_p10": float(np.percentile(attend_ms, 10) * 1e3),
+        "attend_us_p90": float(np.percentile(attend_ms, 90) * 1e3),
+        "keep_fraction": keep_frac,
+        "attend_bytes": attend_bytes,
+        "step_bytes": step_bytes,
+        "tokens": tok_total,
+        "layers_rotated": R,
+        "plan": ffd.plan(shape),
+    }
+
+
+def measure_dense(w, steps, warmup, d, torch, sm_scale):
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+    layer_bytes = (d["k"].numel() + d["v"].numel()) * 2
+    R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
+    ks = [d["k"]] + [d["k"].clone() for _ in range(R - 1)]
+    vs = [d["v"]] + [d["v"].clone() for _ in range(R - 1)]
+    for i in range(warmup):
+        ffd.dense_decode_attn(shape, d["q"], ks[i % R], vs[i % R], d["seq_lens"], sm_scale, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        ffd.dense_decode_attn(shape, d["q"], ks[i % R], vs[i % R], d["seq_lens"], sm_scale, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    byts = DENSE_BYTES * int(d["seq_lens"].sum().item()) * w.kv_heads
+    del ks, vs
+    return {"us_per_step": us, "bytes": byts, "gbps": byts / us / 1e3, "layers_rotated": R}
+
+
+def cpu_baseline(w, delta, c, sm_scale, budget_s=10.0):
+    """The fp64 oracle (as it stands) on the host cores: one decode step of the
+    whole workload (pack excluded), repeated until ~budget_s of CPU work."""
+    from oracle import ffd_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    G = w.group
+    packs = {(b, h): orc.quantize_k(c["k"][b, h]) for b in range(w.batch) for h in range(w.kv_heads)}
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for (b, h), pk in packs.items():
+            orc.decode_head(c["q"][b, h * G:(h + 1) * G], pk, c["v"][b, h], int(c["seq_lens"][b]), delta, sm_scale,
+                            w.sink, w.local)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s and len(times) >= 3:
+            break
+    med = statistics.median(times)
+    return {"value": med * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+            "sample": f"numpy fp64 oracle decode step over all {w.batch * w.kv_heads} KV heads of {w.name} "
+                      f"(delta={delta}, pack excluded), median of {len(times)} steps",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_16k")
+    ap.add_argument("--delta", type=float, default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-long", action="store_true", help="skip the 256K FFD vs dense leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import sparse_long_context_ffd_amd as ffd
+    from synthetic import WORKLOADS
+    ffd.lib()
+    sm_scale = float(np.float32(1.0 / math.sqrt(128.0)))
+    w = WORKLOADS[args.workload]
+    delta = w.deltas[0] if args.delta is None else args.delta
+
+    c, d = prepare(w, args.seed, torch)
+    r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale)
+    dense = measure_dense(w, args.steps, args.warmup, d, torch, sm_scale)
+    achieved = r["attend_bytes"] / (r["attend_us_mean"] * 1e3)
+    result = {
+        "metric": METRIC,
+        "value": round(r["us_per_step"], 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["us_per_step"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "seq_len": int(c["seq_lens"].max()), "delta": delta, "sink": w.sink, "local": w.local,
+                   "head_dim": 128, "block": 64, "keep_fraction": round(r["keep_fraction"], 5),
+                   "layers_rotated": r["layers_rotated"], "chunk_blocks": r["plan"][0]},
+        "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
+        "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
+        "attend_kernel_us": {"mean": round(r["attend_us_mean"], 3), "p10": round(r["attend_us_p10"], 3),
+                             "p90": round(r["attend_us_p90"], 3)},
+        "dense_us_per_step": round(dense["us_per_step"], 3),
+        "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "attend_kernel (fused Top-delta scan + refine)",
+                     "bytes_per_launch": r["attend_bytes"]},
+    }
+    del d
+    torch.cuda.empty_cache()
+
+    if not args.no_long:
+        wl = WORKLOADS["long_256k"]
+        cl, dl = prepare(wl, args.seed, torch)
+        rl = measure_ffd(wl, wl.deltas[0], max(20, args.steps // 4), args.warmup, cl, dl, torch, sm_scale)
+        dn = measure_dense(wl, max(10, args.steps // 8), 5, dl, torch, sm_scale)
+        ach = rl["attend_bytes"] / (rl["attend_us_mean"] * 1e3)
+        result["long_context"] = {
+            "workload": wl.name, "delta": wl.deltas[0], "us_per_step": round(rl["us_per_step"], 3),
+            "keep_fraction": round(rl["keep_fraction"], 5), "attend_kernel_us": round(rl["attend_us_mean"], 3),
+            "effective_gbps": round(rl["step_bytes"] / (rl["us_per_step"] * 1e3), 1),
+            "roofline_attend": {"achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4)},
+            "dense_us_per_step": round(dn["us_per_step"], 3), "dense_gbps": round(dn["gbps"], 1),
+            "speedup_vs_dense": round(dn["us_per_step"] / rl["us_per_step"], 3),
+            "layers_rotated": rl["layers_rotated"], "chunk_blocks": rl["plan"][0],
+        }
+        del dl
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, delta, c, sm_scale)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

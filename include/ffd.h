@@ -1,0 +1,177 @@
+/*
+ * ffd.h -- C ABI of libffd, FFD sparse decode attention for MI355X (gfx950).
+ *
+ * The method is the one summarised in "Faster Than Flash: Exploiting Attention
+ * Sparsity for Efficient Long-Context Decoding" (gist.science technical
+ * summary of arXiv 2609.00097):
+ *   Method 1  K is stored as a 2-bit quantized thumbnail (for score estimates)
+ *             plus 8-bit residuals that rebuild K near fp16;
+ *   Method 2  Top-delta: a token is kept when its score s >= m~ - delta, with the
+ *             pseudo-max m~ taken over the sink and local tokens only;
+ *   Method 3  three stages: pseudo-max estimation, a scan of the 2-bit keys that
+ *             filters blocks against the threshold, and exact attention with the
+ *             residuals and the values on the kept blocks.
+ *
+ * Conventions fixed by this library where the page is silent:
+ *   - head_dim 128, blocks of 64 tokens, 32-channel quantization groups;
+ *   - per token and group: zero = min, scale = fp16 RNE((max-min)/3),
+ *     code c = #{k in 1..3 : x - zero >= (k - 1/2) scale} (0 if scale == 0),
+ *     residual r = x - (zero + c*scale), rscale = fp16 RNE(max|r| / 127),
+ *     res = sign(r) * min(127, #{k >= 1 : |r| >= (k - 1/2) rscale}) (0 if rscale == 0),
+ *     K-hat = zero + c*scale + res*rscale; signed zeros stored as +0;
+ *   - scores are softmax logits s = (q . k) * sm_scale (natural-log units);
+ *     estimated scores use zero + c*scale, exact scores use K-hat;
+ *   - support (pseudo-max) tokens [0, min(sink, L)) U [max(0, L-local), L);
+ *     a block is kept if it holds a support token, or if for some query head h
+ *     of its GQA group  max_{t in block} s_est[h][t] >= m~[h] - delta;
+ *     every query head of the group attends to every valid token of every
+ *     kept block; dropped tokens contribute nothing (softmax renormalised);
+ *   - query head h uses KV head h / (Hq / Hkv).
+ *
+ * Memory: every pointer is a device pointer (hipMalloc / PyTorch CUDA tensor)
+ * unless said otherwise; the caller allocates and frees everything.  Calls
+ * enqueue work on `stream` (a hipStream_t, or NULL for the null stream) and
+ * return without synchronising the host.  The library keeps no state between
+ * calls.  Errors are returned as negative codes; argument checks happen
+ * before any HIP call, so a non-zero return means nothing was enqueued
+ * (except FFD_ERR_HIP, which reports a failed launch).
+ */
+#ifndef FFD_H_
+#define FFD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ffd_status {
+  FFD_OK = 0,
+  FFD_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  FFD_ERR_SHAPE = -2,     /* unsupported shape (see ffd_shape_t)                 */
+  FFD_ERR_ALIGN = -3,     /* a tensor pointer is not 16-byte aligned             */
+  FFD_ERR_DELTA = -4,     /* delta is NaN or -infinity                           */
+  FFD_ERR_WORKSPACE = -5, /* workspace NULL or smaller than ffd_workspace_bytes  */
+  FFD_ERR_ARG = -6,       /* bad scalar argument (token range, sm_scale)         */
+  FFD_ERR_HIP = -7        /* a kernel launch failed                              */
+};
+
+/* Problem shape.  Requirements: batch >= 1, num_kv_heads >= 1,
+ * num_q_heads = G * num_kv_heads with 1 <= G <= 8, head_dim == 128,
+ * block == 64, sink >= 0, local >= 0, sink + local > 0 (the pseudo-max needs
+ * at least one support token), max_seq_len a positive multiple of 64,
+ * chunk_blocks >= 0 (0 = library choice; otherwise the number of 64-token
+ * blocks one work-group scans and refines; it changes only the summation
+ * order of the result). */
+typedef struct ffd_shape {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block;
+  int32_t sink;
+  int32_t local;
+  int32_t max_seq_len;
+  int32_t chunk_blocks;
+} ffd_shape_t;
+
+/* Packed FFD cache of one layer.  nblk = max_seq_len / 64; "head" = (b, kv_head),
+ * head index b * num_kv_heads + kv_head.  Every field is 16-byte aligned.
+ *
+ *  codes   uint8  [B][Hkv][nblk][2048]  2-bit codes.  Token t of a block
+ *          (tt = t/16, tl = t%16), channel slice kq = 0..3, group pair p = 0..1
+ *          own the 32-bit little-endian word at byte
+ *              ((tl*4 + kq)*4 + tt)*8 + p*4
+ *          holding channels 32g + 8kq + j (j = 0..7) of groups g = 2p and 2p+1:
+ *          even g: j = 2d at bit 8+2d,  j = 2d+1 at bit 24+2d   (d = 0..3)
+ *          odd g:  j = 2d at bit 2d,    j = 2d+1 at bit 16+2d.
+ *  sz      fp16   [B][Hkv][nblk][512]   (scale, zero) pairs.  Token t
+ *          (tt = t/16, kq = (t/4)%4, i = t%4), group g: scale at byte
+ *              ((g*4 + kq)*4 + tt)*16 + i*4, zero 2 bytes after it.
+ *  res     int8   [B][Hkv][nblk][8192]  residual of token t, channel ch at byte
+ *              ((ch/16)*64 + t)*16 + ch%16   (two's complement).
+ *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t, group g at
+ *              element t*4 + g.
+ *  v       fp16   [B][Hkv][max_seq_len][128] values, natural row-major layout.
+ *
+ * Positions the pack never wrote (beyond the sequence) may hold any bytes:
+ * decode masks them before any arithmetic that could propagate them. */
+typedef struct ffd_cache {
+  void* codes;
+  void* sz;
+  void* res;
+  void* rscale;
+  const void* v;
+} ffd_cache_t;
+
+/* Optional diagnostic outputs of ffd_decode_attn (each pointer may be NULL).
+ *  m_tilde       f32 [B][Hq]        pseudo-max per query head
+ *  bmax          f32 [B][Hq][nblk]  largest estimated score per block (valid blocks only)
+ *  keep          u8  [B][Hkv][nblk] 1 = block kept (valid blocks only)
+ *  attend_start  hipEvent_t recorded on the stream right before the fused
+ *  attend_stop   scan + refine kernel, and right after it (for timing)       */
+typedef struct ffd_debug {
+  float* m_tilde;
+  float* bmax;
+  uint8_t* keep;
+  void* attend_start;
+  void* attend_stop;
+} ffd_debug_t;
+
+/* Bytes of each packed-cache field for `shape` (host call, no GPU work). */
+int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes,
+                    size_t* res_bytes, size_t* rscale_bytes);
+
+/* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
+ * (host call).  The workspace holds thresholds and per-chunk partials; its
+ * contents need no initialisation. */
+int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
+
+/* Work split chosen for `shape`: blocks per work-group and chunks per
+ * sequence (host call). */
+int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks);
+
+/* K-cache pack (Method 1): quantize tokens [t_begin, t_end) of every (b, kv
+ * head) of `k` (fp16 [B][Hkv][max_seq_len][128]) into `cache` (codes, sz,
+ * res, rscale; cache->v is not used).  0 <= t_begin <= t_end <= max_seq_len;
+ * an empty range is a no-op.  Other positions of the cache are untouched, so
+ * a decode loop appends one token with t_end = t_begin + 1.  K must be finite.
+ * Byte-exact with the conventions above. */
+int ffd_quantize_k(const ffd_shape_t* shape, const void* k, int32_t t_begin, int32_t t_end,
+                   const ffd_cache_t* cache, void* stream);
+
+/* One FFD decode-attention step (Method 3 stages 1-3 plus the log-sum-exp
+ * merge of per-chunk partials).
+ *   q         fp16 [B][Hq][128]
+ *   seq_lens  int32 [B] device array, 1 <= L <= max_seq_len (values outside
+ *             are clamped into that range)
+ *   delta     Top-delta margin in natural-log units; +INFINITY keeps every
+ *             block; NaN and -INFINITY are rejected
+ *   sm_scale  softmax scale, finite and > 0 (usually 1/sqrt(128))
+ *   out       fp16 [B][Hq][128]
+ *   workspace >= ffd_workspace_bytes(shape) bytes, 16-byte aligned
+ *   debug     NULL or diagnostic outputs */
+int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
+                    const int32_t* seq_lens, float delta, float sm_scale, void* out,
+                    void* workspace, size_t workspace_bytes, const ffd_debug_t* debug,
+                    void* stream);
+
+/* Dense flash-decode attention over fp16 K and V ([B][Hkv][max_seq_len][128]),
+ * the speed baseline: out = softmax(q k^T * sm_scale) v over tokens [0, L).
+ * Same argument rules as ffd_decode_attn. */
+int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, float sm_scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Static description of an error code. */
+const char* ffd_strerror(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int ffd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFD_H_ */

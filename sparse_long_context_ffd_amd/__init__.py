@@ -1,0 +1,26 @@
+"""FFD sparse decode attention for MI355X (gfx950): Python binding of libffd.
+
+The compute runs in hand-written HIP kernels behind the C ABI declared in
+``include/ffd.h``; this package only marshals PyTorch tensors into that ABI.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    FFDError,
+    LIB_PATH,
+    PackedCache,
+    Shape,
+    cache_bytes,
+    decode_attn,
+    dense_decode_attn,
+    lib,
+    make_shape,
+    plan,
+    quantize_k,
+    strerror,
+    workspace_bytes,
+)
+
+__all__ = [
+    "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "cache_bytes", "decode_attn",
+    "dense_decode_attn", "lib", "make_shape", "plan", "quantize_k", "strerror", "workspace_bytes",
+]

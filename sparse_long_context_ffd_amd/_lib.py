@@ -1,0 +1,192 @@
+"""ctypes binding of libffd (include/ffd.h).  Argument marshalling only.
+
+Every function forwards to the C entry point of the same name; tensors are
+PyTorch tensors on the GPU and are passed as raw device pointers together with
+the caller's current HIP stream.  There is no CPU fallback: if libffd.so is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libffd.so")
+
+FFD_OK = 0
+STATUS = {
+    0: "FFD_OK", -1: "FFD_ERR_NULL", -2: "FFD_ERR_SHAPE", -3: "FFD_ERR_ALIGN", -4: "FFD_ERR_DELTA",
+    -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP",
+}
+EXPORTED = (
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_decode_attn",
+    "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
+)
+
+
+class FFDError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({strerror(code)})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim", "block", "sink", "local",
+        "max_seq_len", "chunk_blocks")]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("sz", ctypes.c_void_p), ("res", ctypes.c_void_p),
+                ("rscale", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("m_tilde", ctypes.c_void_p), ("bmax", ctypes.c_void_p), ("keep", ctypes.c_void_p),
+                ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libffd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m sparse_long_context_ffd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, V, SZ, I32 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        L.ffd_cache_bytes.argtypes = [P(Shape), P(SZ), P(SZ), P(SZ), P(SZ)]
+        L.ffd_workspace_bytes.argtypes = [P(Shape), P(SZ)]
+        L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
+        L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
+        L.ffd_decode_attn.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, V, V, SZ,
+                                      P(Debug), V]
+        L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
+        L.ffd_strerror.argtypes = [ctypes.c_int]
+        L.ffd_strerror.restype = ctypes.c_char_p
+        L.ffd_version.argtypes = []
+        for n in EXPORTED:
+            if n not in ("ffd_strerror",):
+                getattr(L, n).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().ffd_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != FFD_OK:
+        raise FFDError(code, where)
+
+
+def make_shape(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int, sink: int = 64,
+               local: int = 256, chunk_blocks: int = 0, head_dim: int = 128, block: int = 64) -> Shape:
+    return Shape(batch, num_q_heads, num_kv_heads, head_dim, block, sink, local, max_seq_len, chunk_blocks)
+
+
+def cache_bytes(shape: Shape) -> dict:
+    a, b, c, d = (ctypes.c_size_t() for _ in range(4))
+    _check(lib().ffd_cache_bytes(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                 ctypes.byref(d)), "ffd_cache_bytes")
+    return {"codes": a.value, "sz": b.value, "res": c.value, "rscale": d.value}
+
+
+def workspace_bytes(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ffd_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "ffd_workspace_bytes")
+    return n.value
+
+
+def plan(shape: Shape) -> Tuple[int, int]:
+    cb, nc = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ffd_plan(ctypes.byref(shape), ctypes.byref(cb), ctypes.byref(nc)), "ffd_plan")
+    return cb.value, nc.value
+
+
+# ---------------------------------------------------------------- tensor plumbing
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, dtype, numel, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous() or t.numel() < numel:
+        raise ValueError(f"{name}: expected a contiguous {dtype} CUDA tensor with >= {numel} elements, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+class PackedCache:
+    """Device buffers of one layer's packed FFD cache (plus the caller's fp16 V)."""
+
+    def __init__(self, shape: Shape, v=None, device="cuda"):
+        import torch
+        nb = cache_bytes(shape)
+        self.shape = shape
+        self.codes = torch.empty(nb["codes"], dtype=torch.uint8, device=device)
+        self.sz = torch.empty(nb["sz"], dtype=torch.uint8, device=device)
+        self.res = torch.empty(nb["res"], dtype=torch.uint8, device=device)
+        self.rscale = torch.empty(nb["rscale"], dtype=torch.uint8, device=device)
+        self.v = v
+
+    def fill_(self, byte: int) -> "PackedCache":
+        for t in (self.codes, self.sz, self.res, self.rscale):
+            t.fill_(byte)
+        return self
+
+    def c_struct(self) -> Cache:
+        return Cache(_ptr(self.codes), _ptr(self.sz), _ptr(self.res), _ptr(self.rscale), _ptr(self.v))
+
+
+def quantize_k(shape: Shape, k, t_begin: int, t_end: int, cache: PackedCache, stream=None) -> None:
+    import torch
+    _need(k, torch.float16, shape.batch * shape.num_kv_heads * shape.max_seq_len * 128, "k")
+    c = cache.c_struct()
+    _check(lib().ffd_quantize_k(ctypes.byref(shape), _ptr(k), int(t_begin), int(t_end), ctypes.byref(c),
+                                _stream(stream)), "ffd_quantize_k")
+
+
+def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,
+                workspace, debug: Optional[dict] = None, stream=None) -> None:
+    import torch
+    rows = shape.batch * shape.num_q_heads
+    _need(q, torch.float16, rows * 128, "q")
+    _need(out, torch.float16, rows * 128, "out")
+    _need(seq_lens, torch.int32, shape.batch, "seq_lens")
+    _need(cache.v, torch.float16, shape.batch * shape.num_kv_heads * shape.max_seq_len * 128, "cache.v")
+    _need(workspace, torch.uint8, 0, "workspace")
+    c = cache.c_struct()
+    dbg = None
+    if debug is not None:
+        dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
+                    debug.get("attend_start"), debug.get("attend_stop"))
+    _check(lib().ffd_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
+                                 float(delta), float(sm_scale), _ptr(out), _ptr(workspace),
+                                 workspace.numel(), None if dbg is None else ctypes.byref(dbg),
+                                 _stream(stream)), "ffd_decode_attn")
+
+
+def dense_decode_attn(shape: Shape, q, k, v, seq_lens, sm_scale: float, out, workspace, stream=None) -> None:
+    import torch
+    rows = shape.batch * shape.num_q_heads
+    n = shape.batch * shape.num_kv_heads * shape.max_seq_len * 128
+    _need(q, torch.float16, rows * 128, "q")
+    _need(out, torch.float16, rows * 128, "out")
+    _need(k, torch.float16, n, "k")
+    _need(v, torch.float16, n, "v")
+    _need(seq_lens, torch.int32, shape.batch, "seq_lens")
+    _need(workspace, torch.uint8, 0, "workspace")
+    _check(lib().ffd_dense_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens),
+                                       float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(stream)), "ffd_dense_decode_attn")

@@ -1,0 +1,216 @@
+// C ABI of libffd: argument validation, work split, workspace carving and
+// launches on the caller's stream.  The entry points and their contract are
+// declared and documented in include/ffd.h.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ffd.h"
+#include "ffd_device.h"
+#include "ffd_launch.h"
+
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTargetGroups = 1024;  // work-groups per launch the automatic split aims for
+constexpr int kMaxChunkBlocks = 64;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const ffd_shape_t* s) {
+  if (!s) return FFD_ERR_NULL;
+  if (s->head_dim != 128 || s->block != 64) return FFD_ERR_SHAPE;
+  if (s->batch < 1 || s->num_kv_heads < 1 || s->num_q_heads < 1) return FFD_ERR_SHAPE;
+  if (s->num_q_heads % s->num_kv_heads != 0) return FFD_ERR_SHAPE;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (G < 1 || G > ffd::kMaxG) return FFD_ERR_SHAPE;
+  if (s->sink < 0 || s->local < 0 || s->chunk_blocks < 0) return FFD_ERR_SHAPE;
+  if (s->sink == 0 && s->local == 0) return FFD_ERR_SHAPE;  // the pseudo-max needs a support set
+  if (s->max_seq_len < 64 || s->max_seq_len % 64 != 0) return FFD_ERR_SHAPE;
+  return FFD_OK;
+}
+
+struct Plan {
+  int nblk_cap, cb, nchunk;
+  size_t thr_off, ml_off, o_off, total;
+};
+
+Plan make_plan(const ffd_shape_t* s) {
+  Plan p;
+  p.nblk_cap = s->max_seq_len / 64;
+  if (s->chunk_blocks > 0) {
+    p.cb = s->chunk_blocks < p.nblk_cap ? s->chunk_blocks : p.nblk_cap;
+  } else {
+    const long long total = (long long)s->batch * s->num_kv_heads * p.nblk_cap;
+    long long cb = (total + kTargetGroups - 1) / kTargetGroups;
+    if (cb < 1) cb = 1;
+    if (cb > kMaxChunkBlocks) cb = kMaxChunkBlocks;
+    p.cb = (int)cb;
+  }
+  p.nchunk = (p.nblk_cap + p.cb - 1) / p.cb;
+  const size_t rows = (size_t)s->batch * s->num_q_heads;
+  p.thr_off = 0;
+  p.ml_off = round_up(rows * sizeof(float), kAlign);
+  p.o_off = p.ml_off + round_up(rows * p.nchunk * 2 * sizeof(float), kAlign);
+  p.total = p.o_off + round_up(rows * p.nchunk * 128 * sizeof(float), kAlign);
+  return p;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ffd_version(void) { return 100; }
+
+const char* ffd_strerror(int code) {
+  switch (code) {
+    case FFD_OK: return "ok";
+    case FFD_ERR_NULL: return "required pointer is NULL";
+    case FFD_ERR_SHAPE: return "unsupported shape (head_dim 128, block 64, Hq = G*Hkv with G <= 8, max_seq_len multiple of 64)";
+    case FFD_ERR_ALIGN: return "tensor pointer is not 16-byte aligned";
+    case FFD_ERR_DELTA: return "delta is NaN or -infinity";
+    case FFD_ERR_WORKSPACE: return "workspace missing or too small";
+    case FFD_ERR_ARG: return "bad scalar argument (token range or sm_scale)";
+    case FFD_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown ffd status code";
+  }
+}
+
+int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes, size_t* res_bytes,
+                    size_t* rscale_bytes) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!codes_bytes || !sz_bytes || !res_bytes || !rscale_bytes) return FFD_ERR_NULL;
+  const size_t blocks = (size_t)shape->batch * shape->num_kv_heads * (shape->max_seq_len / 64);
+  *codes_bytes = blocks * ffd::kCodesBytes;
+  *sz_bytes = blocks * ffd::kSzBytes;
+  *res_bytes = blocks * ffd::kResBytes;
+  *rscale_bytes = blocks * ffd::kRscBytes;
+  return FFD_OK;
+}
+
+int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!bytes) return FFD_ERR_NULL;
+  *bytes = make_plan(shape).total;
+  return FFD_OK;
+}
+
+int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!chunk_blocks || !n_chunks) return FFD_ERR_NULL;
+  const Plan p = make_plan(shape);
+  *chunk_blocks = p.cb;
+  *n_chunks = p.nchunk;
+  return FFD_OK;
+}
+
+int ffd_quantize_k(const ffd_shape_t* shape, const void* k, int32_t t_begin, int32_t t_end,
+                   const ffd_cache_t* cache, void* stream) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!k || !cache || !cache->codes || !cache->sz || !cache->res || !cache->rscale) return FFD_ERR_NULL;
+  if (!aligned16(k) || !aligned16(cache->codes) || !aligned16(cache->sz) || !aligned16(cache->res) ||
+      !aligned16(cache->rscale))
+    return FFD_ERR_ALIGN;
+  if (t_begin < 0 || t_end < t_begin || t_end > shape->max_seq_len) return FFD_ERR_ARG;
+  if (t_end == t_begin) return FFD_OK;
+  return from_hip(ffd::launch_pack(k, shape->batch, shape->num_kv_heads, shape->max_seq_len, t_begin, t_end,
+                                   cache->codes, cache->sz, cache->res, cache->rscale,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
+                    float delta, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
+                    const ffd_debug_t* debug, void* stream) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!q || !cache || !seq_lens || !out || !cache->codes || !cache->sz || !cache->res || !cache->rscale ||
+      !cache->v)
+    return FFD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(cache->codes) || !aligned16(cache->sz) ||
+      !aligned16(cache->res) || !aligned16(cache->rscale) || !aligned16(cache->v) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FFD_ERR_ALIGN;
+  if (isnan(delta) || (isinf(delta) && delta < 0)) return FFD_ERR_DELTA;
+  if (!(sm_scale > 0.f) || isinf(sm_scale)) return FFD_ERR_ARG;
+  const Plan pl = make_plan(shape);
+  if (!workspace || workspace_bytes < pl.total) return FFD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FFD_ERR_ALIGN;
+
+  ffd::DecodeParams p = {};
+  char* ws = static_cast<char*>(workspace);
+  p.q = static_cast<const uint16_t*>(q);
+  p.codes = static_cast<const uint8_t*>(cache->codes);
+  p.sz = static_cast<const uint8_t*>(cache->sz);
+  p.res = static_cast<const int8_t*>(cache->res);
+  p.rsc = static_cast<const uint8_t*>(cache->rscale);
+  p.v = static_cast<const uint16_t*>(cache->v);
+  p.seq_lens = seq_lens;
+  p.thr = reinterpret_cast<float*>(ws + pl.thr_off);
+  p.part_ml = reinterpret_cast<float2*>(ws + pl.ml_off);
+  p.part_o = reinterpret_cast<float*>(ws + pl.o_off);
+  if (debug) {
+    p.dbg_mt = debug->m_tilde;
+    p.dbg_bmax = debug->bmax;
+    p.dbg_keep = debug->keep;
+    p.ev_start = static_cast<hipEvent_t>(debug->attend_start);
+    p.ev_stop = static_cast<hipEvent_t>(debug->attend_stop);
+  }
+  p.out = static_cast<uint16_t*>(out);
+  p.B = shape->batch;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.L_cap = shape->max_seq_len;
+  p.nblk_cap = pl.nblk_cap;
+  p.nchunk = pl.nchunk;
+  p.cb = pl.cb;
+  p.sink = shape->sink;
+  p.local = shape->local;
+  p.delta = delta;
+  p.sm_scale = sm_scale;
+  return from_hip(ffd::launch_ffd_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, float sm_scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!q || !k || !v || !seq_lens || !out) return FFD_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return FFD_ERR_ALIGN;
+  if (!(sm_scale > 0.f) || isinf(sm_scale)) return FFD_ERR_ARG;
+  const Plan pl = make_plan(shape);
+  if (!workspace || workspace_bytes < pl.total) return FFD_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FFD_ERR_ALIGN;
+  ffd::DecodeParams p = {};
+  char* ws = static_cast<char*>(workspace);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.seq_lens = seq_lens;
+  p.thr = reinterpret_cast<float*>(ws + pl.thr_off);
+  p.part_ml = reinterpret_cast<float2*>(ws + pl.ml_off);
+  p.part_o = reinterpret_cast<float*>(ws + pl.o_off);
+  p.out = static_cast<uint16_t*>(out);
+  p.B = shape->batch;
+  p.Hq = shape->num_q_heads;
+  p.Hkv = shape->num_kv_heads;
+  p.L_cap = shape->max_seq_len;
+  p.nblk_cap = pl.nblk_cap;
+  p.nchunk = pl.nchunk;
+  p.cb = pl.cb;
+  p.sm_scale = sm_scale;
+  return from_hip(ffd::launch_dense_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Device-side helpers shared by the FFD kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffd {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 64;
+constexpr int kGroup = 32;
+constexpr int kGroups = 4;
+constexpr int kMaxG = 8;                // query heads per KV head supported
+constexpr int kCodesBytes = 2048;       // per 64-token block and head
+constexpr int kSzBytes = 1024;
+constexpr int kResBytes = 8192;
+constexpr int kRscBytes = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// packed-cache layout (byte offsets inside one 64-token block of one head)
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int codes_word_off(int t, int kq, int p) {
+  return (((t & 15) * 4 + kq) * 4 + (t >> 4)) * 8 + p * 4;
+}
+__host__ __device__ inline int sz_off(int t, int g) {
+  return ((g * 4 + ((t >> 2) & 3)) * 4 + (t >> 4)) * 16 + (t & 3) * 4;
+}
+__host__ __device__ inline int res_off(int t, int ch) { return ((ch >> 4) * 64 + t) * 16 + (ch & 15); }
+__host__ __device__ inline int rsc_off(int t, int g) { return (t * 4 + g) * 2; }
+// bit of channel (32g + 8kq + j) inside its word
+__host__ __device__ inline int code_bit(int g, int j) {
+  const int d = j >> 1;
+  return (g & 1) ? ((j & 1) ? 16 + 2 * d : 2 * d) : ((j & 1) ? 24 + 2 * d : 8 + 2 * d);
+}
+
+// ---------------------------------------------------------------------------
+// small conversions
+// ---------------------------------------------------------------------------
+__device__ inline float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ inline float lo_h(uint32_t w) { return h2f((uint16_t)(w & 0xffffu)); }
+__device__ inline float hi_h(uint32_t w) { return h2f((uint16_t)(w >> 16)); }
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions (wave64)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ inline float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// maximum over all 64 lanes, returned in every lane
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// sum over all 64 lanes, returned in every lane
+__device__ inline float wave_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ inline float uniform_lane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+}  // namespace ffd

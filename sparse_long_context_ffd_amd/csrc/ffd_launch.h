@@ -1,0 +1,36 @@
+// Kernel parameter block and host-side launchers (internal to libffd).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffd {
+
+struct DecodeParams {
+  const uint16_t* q;       // [B][Hq][128] fp16
+  const uint8_t* codes;    // packed cache fields (layouts in include/ffd.h)
+  const uint8_t* sz;
+  const int8_t* res;
+  const uint8_t* rsc;
+  const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
+  const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]
+  const int32_t* seq_lens; // [B]
+  float* thr;              // [B][Hq]
+  float* part_o;           // [B][Hq][nchunk][128]
+  float2* part_ml;         // [B][Hq][nchunk] (m, l)
+  float* dbg_mt;           // optional [B][Hq]
+  float* dbg_bmax;         // optional [B][Hq][nblk_cap]
+  uint8_t* dbg_keep;       // optional [B][Hkv][nblk_cap]
+  uint16_t* out;           // [B][Hq][128] fp16
+  hipEvent_t ev_start;     // optional, recorded around the attend kernel
+  hipEvent_t ev_stop;
+  int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, sink, local;
+  float delta, sm_scale;
+};
+
+hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, int t_end, void* codes,
+                       void* sz, void* res, void* rsc, hipStream_t stream);
+hipError_t launch_ffd_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_dense_decode(const DecodeParams& p, hipStream_t s);
+
+}  // namespace ffd

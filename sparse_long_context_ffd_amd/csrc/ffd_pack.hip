@@ -1,0 +1,162 @@
+// K-cache pack: fp16 keys -> 2-bit thumbnail (codes + fp16 scale/zero) and
+// int8 residual (+ fp16 residual scale), per token and 32-channel group.
+//
+// Follows "Faster Than Flash" (gist.science summary of arXiv 2609.00097),
+// Method section 1: the K cache is split into a 2-bit quantized thumbnail used
+// to estimate scores and 8-bit residuals that rebuild K close to fp16.  The
+// page gives no quantizer; the convention implemented here is documented in
+// include/ffd.h.  Every decision is an exact fp64 comparison: fp16 inputs,
+// their differences, code*scale products and (k +- 1/2)*scale thresholds are
+// all exactly representable in fp64, and the two divisions are correctly
+// rounded in fp64 and then rounded once more to fp16 with integer logic (the
+// fp64 quotient is never close enough to an fp16 rounding midpoint for that
+// double rounding to differ from rounding the exact quotient).
+//
+// Launch: grid (ceil(n/64), Hkv, B), 256 threads; thread = (token, group),
+// 4 threads per token, 64 tokens per work-group.
+#include "ffd_device.h"
+#include "ffd_launch.h"
+
+namespace ffd {
+
+// round a finite double (|x| < 65520) to fp16 bits, nearest-even
+__device__ inline uint16_t f64_to_f16_rne(double x) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+  const uint16_t sign = (uint16_t)((bits >> 48) & 0x8000u);
+  const uint64_t mag = bits & 0x7fffffffffffffffull;
+  if (mag == 0) return sign;
+  const int e = (int)(mag >> 52) - 1023;  // inputs here are normal doubles
+  const uint64_t m = (mag & ((1ull << 52) - 1)) | (1ull << 52);
+  const int shift = (e >= -14) ? 42 : 42 + (-14 - e);
+  if (shift >= 54) return sign;  // below 2^-25: rounds to zero
+  uint64_t kept = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (kept & 1))) ++kept;
+  if (e >= -14) {
+    int ee = e;
+    if (kept == 2048) { kept = 1024; ++ee; }
+    if (ee > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | ((ee + 15) << 10) | (uint16_t)(kept - 1024));
+  }
+  return (uint16_t)(sign | (uint16_t)kept);  // subnormal (kept == 1024 is the smallest normal)
+}
+
+__device__ inline double f16bits_to_f64(uint16_t b) {
+  return (double)__builtin_bit_cast(_Float16, b);
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ k, int L_cap,
+                                                   int t_begin, int t_end,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint32_t* __restrict__ sz,
+                                                   int8_t* __restrict__ res,
+                                                   uint16_t* __restrict__ rsc) {
+  const int tid = threadIdx.x;
+  const int g = tid & 3;
+  const int t = t_begin + blockIdx.x * 64 + (tid >> 2);
+  const bool active = t < t_end;
+  const size_t head = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int nblk_cap = L_cap >> 6;
+  const int tc = active ? t : t_begin;  // inactive threads read a valid row and store nothing
+
+  // 32 fp16 values of this (token, group)
+  const uint4* src = reinterpret_cast<const uint4*>(k + (head * L_cap + tc) * kHeadDim + g * kGroup);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  double x[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[2 * i] = f16bits_to_f64((uint16_t)(w[i] & 0xffffu));
+    x[2 * i + 1] = f16bits_to_f64((uint16_t)(w[i] >> 16));
+  }
+  double mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) { mn = fmin(mn, x[i]); mx = fmax(mx, x[i]); }
+  mn = mn + 0.0;  // -0 -> +0
+  const uint16_t zb = f64_to_f16_rne(mn);
+  const uint16_t sb = f64_to_f16_rne((mx - mn) / 3.0 + 0.0);
+  const double s = f16bits_to_f64(sb);
+
+  int c[32];
+  double amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double d = x[i] - mn;
+    int ci = 0;
+    if (s > 0.0) ci = (d >= 0.5 * s) + (d >= 1.5 * s) + (d >= 2.5 * s);
+    c[i] = ci;
+    x[i] = x[i] - (mn + ci * s);  // residual, exact
+    amax = fmax(amax, fabs(x[i]));
+  }
+  const uint16_t s8b = f64_to_f16_rne(amax / 127.0);
+  const double s8 = f16bits_to_f64(s8b);
+
+  uint32_t rw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rw[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int e = 0;
+    if (s8 > 0.0) {
+      const double a = fabs(x[i]);
+      double kf = floor(a / s8 + 0.5);
+      if (a >= (kf + 0.5) * s8) kf += 1.0;
+      if (kf > 0.0 && a < (kf - 0.5) * s8) kf -= 1.0;
+      kf = fmin(kf, 127.0);
+      e = (int)kf;
+      if (x[i] < 0.0) e = -e;
+    }
+    rw[i >> 2] |= ((uint32_t)(e & 0xff)) << (8 * (i & 3));
+  }
+
+  // code fragments of this group for the four channel slices kq
+  uint32_t frag[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    uint32_t f = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f |= (uint32_t)c[8 * kq + j] << code_bit(g, j);
+    frag[kq] = f;
+  }
+  uint32_t other[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) other[kq] = (uint32_t)__shfl_xor((int)frag[kq], 1, 64);
+
+  if (!active) return;
+  const int blk = t >> 6, tb = t & 63;
+  const size_t blk_idx = head * nblk_cap + blk;
+  uint8_t* cbase = reinterpret_cast<uint8_t*>(codes) + blk_idx * kCodesBytes;
+  const int p = g >> 1;
+  // even group writes slices 0,1; odd group writes slices 2,3 of the shared words
+  const int kq0 = (g & 1) ? 2 : 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int kq = kq0 + u;
+    *reinterpret_cast<uint32_t*>(cbase + codes_word_off(tb, kq, p)) = frag[kq] | other[kq];
+  }
+  uint8_t* zbase = reinterpret_cast<uint8_t*>(sz) + blk_idx * kSzBytes;
+  *reinterpret_cast<uint32_t*>(zbase + sz_off(tb, g)) = (uint32_t)sb | ((uint32_t)zb << 16);
+  int8_t* rbase = res + blk_idx * kResBytes;
+  *reinterpret_cast<uint4*>(rbase + res_off(tb, 32 * g)) = make_uint4(rw[0], rw[1], rw[2], rw[3]);
+  *reinterpret_cast<uint4*>(rbase + res_off(tb, 32 * g + 16)) = make_uint4(rw[4], rw[5], rw[6], rw[7]);
+  uint8_t* sbase = reinterpret_cast<uint8_t*>(rsc) + blk_idx * kRscBytes;
+  *reinterpret_cast<uint16_t*>(sbase + rsc_off(tb, g)) = s8b;
+}
+
+hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, int t_end, void* codes,
+                       void* sz, void* res, void* rsc, hipStream_t stream) {
+  const int n = t_end - t_begin;
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 63) / 64, Hkv, B);
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(k), L_cap,
+                     t_begin, t_end, static_cast<uint32_t*>(codes), static_cast<uint32_t*>(sz),
+                     static_cast<int8_t*>(res), static_cast<uint16_t*>(rsc));
+  return hipGetLastError();
+}
+
+}  // namespace ffd

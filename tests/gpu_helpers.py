@@ -1,0 +1,127 @@
+"""Shared helpers of the GPU parity tests: run libffd through its binding and
+compare with the fp64 oracle by the parity rules.
+
+Parity rules
+------------
+* packed codes, fp16 scale/zero, int8 residuals and fp16 residual scales:
+  bit-exact;
+* block mask: equal to the oracle's on every *pinned* block -- forced blocks,
+  blocks where some head's oracle block max is >= its threshold + 1e-4, and
+  blocks where every head's oracle block max is < its threshold - 1e-4;
+  blocks within 1e-4 of a threshold are exempt (either choice is correct);
+* attention output: compared with the oracle evaluated under the GPU's own
+  mask: max |diff| <= 2e-3 and ||diff|| / ||ref|| <= 1e-3 (fp16 output).
+"""
+import math
+import sys
+
+import numpy as np
+
+BAND = 1e-4
+ATOL = 2e-3
+RTOL_L2 = 1e-3
+SM_SCALE = float(np.float32(1.0 / math.sqrt(128.0)))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        import pytest
+        pytest.skip("no GPU")
+    return torch
+
+
+def dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def shape_for(w, chunk_blocks=0, sink=None, local=None):
+    import sparse_long_context_ffd_amd as ffd
+    return ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len,
+                          sink=w.sink if sink is None else sink,
+                          local=w.local if local is None else local, chunk_blocks=chunk_blocks)
+
+
+def gpu_pack(shape, k_dev, fill=0xFF, t_begin=0, t_end=None):
+    """Pack [t_begin, t_end) into a fresh cache whose bytes start as `fill`."""
+    import sparse_long_context_ffd_amd as ffd
+    cache = ffd.PackedCache(shape).fill_(fill)
+    ffd.quantize_k(shape, k_dev, t_begin, shape.max_seq_len if t_end is None else t_end, cache)
+    return cache
+
+
+def decode_cache_fields(cache, w):
+    from tests.layout import decode_cache
+    return decode_cache(**cache_to_host(cache), B=w.batch, Hkv=w.kv_heads, L_cap=w.max_len)
+
+
+def cache_to_host(cache):
+    return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale")}
+
+
+def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE):
+    import sparse_long_context_ffd_amd as ffd
+    B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
+    nb = shape.max_seq_len // 64
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    dbg = {
+        "m_tilde": torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda"),
+        "bmax": torch.full((B, Hq, nb), float("nan"), dtype=torch.float32, device="cuda"),
+        "keep": torch.full((B, Hkv, nb), 7, dtype=torch.uint8, device="cuda"),
+    }
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg)
+    torch.cuda.synchronize()
+    return {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
+
+
+def gpu_dense(shape, q_dev, k_dev, v_dev, lens_dev, torch, sm_scale=SM_SCALE):
+    import sparse_long_context_ffd_amd as ffd
+    out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float16, device="cuda")
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    ffd.dense_decode_attn(shape, q_dev, k_dev, v_dev, lens_dev, sm_scale, out, ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def mask_pins(o):
+    """(pinned_keep, pinned_drop) boolean [nblk] from an oracle decode_head result."""
+    bmax, thr = o["bmax"], o["thr"][:, None]
+    pk = o["forced"] | (bmax >= thr + BAND).any(axis=0)
+    pd = (~o["forced"]) & (bmax < thr - BAND).all(axis=0)
+    return pk, pd
+
+
+def check_head(orc, q16, pk_head, V16, L, delta, got, b, h, G, sink=64, local=256, sm_scale=SM_SCALE,
+               label=""):
+    """Compare one (b, kv head) of a GPU decode with the oracle; returns stats."""
+    nb = (L + 63) // 64
+    o = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local)
+    keep = got["keep"][b, h, :nb].astype(bool)
+    assert set(np.unique(got["keep"][b, h, :nb]).tolist()) <= {0, 1}, f"{label} keep flags not 0/1"
+    pk, pd = mask_pins(o)
+    bad_keep = np.nonzero(pk & ~keep)[0]
+    bad_drop = np.nonzero(pd & keep)[0]
+    assert bad_keep.size == 0 and bad_drop.size == 0, \
+        f"{label} mask mismatch on pinned blocks: missing {bad_keep[:10]}, extra {bad_drop[:10]}"
+    mt = got["m_tilde"][b, h * G:(h + 1) * G]
+    mt_err = float(np.abs(mt - o["m_tilde"]).max())
+    bm = got["bmax"][b, h * G:(h + 1) * G, :nb]
+    bm_err = float(np.abs(bm - o["bmax"]).max())
+    assert mt_err <= BAND, f"{label} pseudo-max error {mt_err}"
+    assert bm_err <= BAND, f"{label} block-max error {bm_err}"
+    ref = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local, keep=keep)["out"]
+    g_out = got["out"][b, h * G:(h + 1) * G]
+    d = g_out - ref
+    max_abs = float(np.abs(d).max())
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
+    rmse = float(np.sqrt(np.mean(d * d)))
+    assert max_abs <= ATOL and rel <= RTOL_L2, f"{label} output max-abs {max_abs} rel-L2 {rel}"
+    return {"keep_frac": float(keep.mean()), "exempt": int(nb - pk.sum() - pd.sum()),
+            "mt_err": mt_err, "bmax_err": bm_err, "max_abs": max_abs, "rel_l2": rel, "rmse": rmse,
+            "mask_equal": bool((keep == o["keep"]).all())}

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: exports, argument validation, planning, layout maps.
+
+Every call here fails validation (or is a pure host query) before any HIP
+call, so nothing touches a device.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_long_context_ffd_amd as ffd
+from sparse_long_context_ffd_amd import _lib
+from tests import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED)
+    L = ffd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ffd_version() == 100
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -8, -1):
+        assert "unknown" not in ffd.strerror(code)
+    assert "unknown" in ffd.strerror(-99)
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every call below fails validation first
+
+
+def _ws(shape):
+    return ffd.workspace_bytes(shape)
+
+
+def _decode(shape, q=FAKE, cache=None, lens=FAKE, delta=5.0, scale=0.088, out=FAKE, ws=FAKE, wsb=None):
+    c = cache or _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return ffd.lib().ffd_decode_attn(None if shape is None else ctypes.byref(shape), q, ctypes.byref(c), lens,
+                                     delta, scale, out, ws, _ws(shape) if wsb is None else wsb, None, None)
+
+
+def test_shape_validation():
+    good = ffd.make_shape(1, 32, 8, 16384)
+    assert ffd.workspace_bytes(good) > 0
+    bad = [
+        dict(head_dim=64), dict(block=32), dict(num_q_heads=30), dict(num_q_heads=72),  # G = 9
+        dict(max_seq_len=1000), dict(max_seq_len=0), dict(sink=-1), dict(local=-1),
+        dict(sink=0, local=0), dict(chunk_blocks=-2), dict(batch=0), dict(num_kv_heads=0),
+    ]
+    for kw in bad:
+        args = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384)
+        args.update(kw)
+        s = ffd.make_shape(**{k: v for k, v in args.items() if k in ("batch", "num_q_heads", "num_kv_heads",
+                                                                     "max_seq_len", "sink", "local",
+                                                                     "chunk_blocks", "head_dim", "block")})
+        n = ctypes.c_size_t()
+        assert ffd.lib().ffd_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == -2, kw
+        assert _decode(s, wsb=1 << 30) == -2, kw
+    assert ffd.lib().ffd_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == -1
+
+
+def test_decode_argument_errors():
+    s = ffd.make_shape(1, 32, 8, 16384)
+    assert _decode(s, q=None) == -1
+    assert _decode(s, out=None) == -1
+    assert _decode(s, lens=None) == -1
+    assert _decode(s, cache=_lib.Cache(FAKE, FAKE, FAKE, FAKE, None)) == -1
+    assert _decode(s, q=FAKE + 8) == -3
+    assert _decode(s, cache=_lib.Cache(FAKE, FAKE + 4, FAKE, FAKE, FAKE)) == -3
+    assert _decode(s, lens=FAKE + 2) == -3
+    assert _decode(s, delta=math.nan) == -4
+    assert _decode(s, delta=-math.inf) == -4
+    assert _decode(s, scale=0.0) == -6
+    assert _decode(s, scale=-1.0) == -6
+    assert _decode(s, scale=math.inf) == -6
+    assert _decode(s, scale=math.nan) == -6
+    assert _decode(s, wsb=_ws(s) - 1) == -5
+    assert _decode(s, ws=None) == -5
+    assert _decode(s, ws=FAKE + 8) == -3
+
+
+def test_dense_and_pack_argument_errors():
+    s = ffd.make_shape(2, 8, 2, 4096)
+    L = ffd.lib()
+    wsb = _ws(s)
+    assert L.ffd_dense_decode_attn(ctypes.byref(s), FAKE, None, FAKE, FAKE, 0.1, FAKE, FAKE, wsb, None) == -1
+    assert L.ffd_dense_decode_attn(ctypes.byref(s), FAKE, FAKE + 2, FAKE, FAKE, 0.1, FAKE, FAKE, wsb, None) == -3
+    assert L.ffd_dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, FAKE, wsb, None) == -6
+    assert L.ffd_dense_decode_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, wsb - 1, None) == -5
+    c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, None)
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE, -1, 5, ctypes.byref(c), None) == -6
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE, 6, 5, ctypes.byref(c), None) == -6
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE, 0, 4097, ctypes.byref(c), None) == -6
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE, 10, 10, ctypes.byref(c), None) == 0   # empty range: no-op
+    assert L.ffd_quantize_k(ctypes.byref(s), None, 0, 5, ctypes.byref(c), None) == -1
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE + 6, 0, 5, ctypes.byref(c), None) == -3
+    assert L.ffd_quantize_k(ctypes.byref(s), FAKE, 0, 5, ctypes.byref(_lib.Cache(FAKE, None, FAKE, FAKE, None)),
+                            None) == -1
+
+
+def test_cache_and_workspace_sizes():
+    s = ffd.make_shape(2, 28, 4, 32768)
+    nb = ffd.cache_bytes(s)
+    blocks = 2 * 4 * 512
+    assert nb == {"codes": blocks * 2048, "sz": blocks * 1024, "res": blocks * 8192, "rscale": blocks * 512}
+    per_token = sum(nb.values()) / (2 * 4 * 32768)
+    assert per_token == 184          # 2-bit codes 32 + (scale, zero) 16 + int8 residual 128 + rscale 8
+    cb, nch = ffd.plan(s)
+    assert nch == math.ceil(512 / cb)
+    rows = 2 * 28
+    need = rows * 4 + rows * nch * 8 + rows * nch * 128 * 4
+    assert need <= ffd.workspace_bytes(s) <= need + 3 * 256
+
+
+@pytest.mark.parametrize("B,Hkv,L,expect", [(1, 8, 16384, 2), (1, 8, 262144, 32), (16, 4, 32768, 32),
+                                            (1, 1, 4096, 1), (4, 8, 131072, 64)])
+def test_automatic_split(B, Hkv, L, expect):
+    cb, nch = ffd.plan(ffd.make_shape(B, Hkv, Hkv, L))
+    assert cb == expect and nch == math.ceil(L // 64 / cb)
+    cb, nch = ffd.plan(ffd.make_shape(B, Hkv, Hkv, L, chunk_blocks=10 ** 6))
+    assert cb == L // 64 and nch == 1
+
+
+def test_layout_maps_are_bijective():
+    """Each code bit, (scale, zero) slot and residual byte of a block is used exactly once."""
+    bits = layout._WORD * 32 + layout._BIT
+    assert np.unique(np.concatenate([bits.ravel(), bits.ravel() + 1])).size == 64 * 128 * 2
+    assert (layout._BIT % 2 == 0).all() and layout._WORD.max() == 511
+    sz = layout._SZ
+    assert np.unique(np.concatenate([sz.ravel(), sz.ravel() + 1])).size == 512
+    assert np.unique(layout._RES).size == 8192 and layout._RES.max() == 8191
+    assert np.unique(layout._RSC).size == 256

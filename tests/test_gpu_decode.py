@@ -1,0 +1,133 @@
+"""GPU parity of one FFD decode step (ffd_decode_attn) against the fp64 oracle.
+
+Mask: equal on every pinned block; output: within max-abs 2e-3 and rel-L2
+1e-3 of the oracle evaluated under the GPU's mask (rules in gpu_helpers).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import ffd_oracle as orc
+from synthetic import WORKLOADS, Workload, make_case
+from tests.gpu_helpers import (SM_SCALE, check_head, dev, gpu_decode, gpu_dense, gpu_pack, say,
+                               shape_for, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, seed, deltas, heads=None, chunk_blocks=0, sink=None, local=None, fill=0xFF):
+    torch = torch_mod()
+    c = make_case(w, seed, heads=heads)
+    shape = shape_for(w, chunk_blocks, sink, local)
+    S = w.sink if sink is None else sink
+    W = w.local if local is None else local
+    qd, kd, vd = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
+    ld = dev(c["seq_lens"], torch)
+    cache = gpu_pack(shape, kd, fill=fill)
+    cache.v = vd
+    G = w.group
+    todo = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    stats = []
+    for delta in deltas:
+        say(f"decode {w.name} seed={seed} delta={delta} cb={chunk_blocks} sink={S} local={W} heads={todo}")
+        got = gpu_decode(shape, qd, cache, ld, delta, torch)
+        for b, h in todo:
+            L = int(c["seq_lens"][b])
+            pk = orc.quantize_k(c["k"][b, h])
+            st = check_head(orc, c["q"][b, h * G:(h + 1) * G], pk, c["v"][b, h], L, delta, got, b, h, G,
+                            sink=S, local=W, label=f"{w.name} s{seed} d{delta} b{b} h{h}")
+            st.update(delta=delta, b=b, h=h)
+            stats.append(st)
+    for s in stats:
+        say("  ", {k: (round(v, 7) if isinstance(v, float) else v) for k, v in s.items()})
+    return stats
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_decode_tiny(seed):
+    st = _run(WORKLOADS["tiny_h4x1_4k"], seed, [5.0, 7.0, math.inf, -1e30])
+    assert all(s["keep_frac"] == 1.0 for s in st if s["delta"] == math.inf)
+
+
+def test_decode_llama8b_16k_all_heads():
+    st = _run(WORKLOADS["llama8b_16k"], 0, [5.0, 7.0])
+    kf = np.mean([s["keep_frac"] for s in st if s["delta"] == 5.0])
+    say(f"llama8b_16k keep fraction at delta=5: {kf:.3f}")
+    assert 0.0 < kf < 1.0
+
+
+def test_decode_qwen_batched_sampled():
+    _run(WORKLOADS["qwen7b_b16_16k32k"], 0, [7.0, 3.0], heads=[(0, 0), (5, 3), (15, 1)])
+
+
+@pytest.mark.parametrize("cb", [1, 3, 16])
+def test_decode_chunking_invariance(cb):
+    """The work split changes only the summation order."""
+    _run(WORKLOADS["tiny_h4x1_4k"], 1, [5.0], chunk_blocks=cb)
+
+
+@pytest.mark.parametrize("G,L", [(1, 1), (2, 63), (3, 64), (5, 65), (6, 320), (7, 321), (8, 1000), (4, 4031)])
+def test_decode_group_sizes_and_ragged_lengths(G, L):
+    """Every supported GQA group size, partial last blocks, L <= sink+local, NaN-filled cache tails."""
+    w = Workload(f"g{G}_l{L}", 2, 2 * G, 2, 4096, L, deltas=(3.0,), needles=4)
+    _run(w, 0, [3.0, 0.5], fill=0xFF)
+
+
+def test_decode_sink_and_local_variants():
+    w = WORKLOADS["tiny_h4x1_4k"]
+    _run(w, 2, [2.0], sink=0, local=64)
+    _run(w, 2, [2.0], sink=130, local=0)
+    _run(w, 2, [2.0], sink=0, local=1)
+
+
+def test_decode_variable_lengths_in_batch():
+    w = Workload("varlen", 4, 8, 2, 2048, None, len_range=(1, 2048), deltas=(4.0,), needles=3)
+    _run(w, 5, [4.0])
+
+
+def test_dense_matches_oracle():
+    torch = torch_mod()
+    for w, heads in [(WORKLOADS["tiny_h4x1_4k"], None), (WORKLOADS["llama8b_16k"], [(0, 1), (0, 6)]),
+                     (Workload("dense_g7", 3, 14, 2, 1024, None, len_range=(1, 1024)), None)]:
+        say(f"dense {w.name}")
+        c = make_case(w, 0, heads=heads)
+        shape = shape_for(w)
+        out = gpu_dense(shape, dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch),
+                        dev(c["seq_lens"], torch), torch)
+        todo = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+        G = w.group
+        for b, h in todo:
+            L = int(c["seq_lens"][b])
+            ref = orc.dense_head(c["q"][b, h * G:(h + 1) * G], c["k"][b, h], c["v"][b, h], L, SM_SCALE)
+            d = out[b, h * G:(h + 1) * G] - ref
+            ma, rel = float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
+            say(f"  dense b{b} h{h} L{L} max_abs={ma:.2e} rel={rel:.2e}")
+            assert ma <= 2e-3 and rel <= 1e-3
+
+
+def test_infinite_delta_equals_dense_over_khat():
+    """delta = +inf keeps every block; the result is dense attention over K-hat."""
+    torch = torch_mod()
+    w = WORKLOADS["tiny_h4x1_4k"]
+    c = make_case(w, 0)
+    shape = shape_for(w)
+    cache = gpu_pack(shape, dev(c["k"], torch))
+    cache.v = dev(c["v"], torch)
+    got = gpu_decode(shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), math.inf, torch)
+    assert (got["keep"][0, 0, :64] == 1).all()
+    _, khat = orc.dequantize(orc.quantize_k(c["k"][0, 0]))
+    ref = orc.dense_head(c["q"][0], khat, c["v"][0, 0], 4096, SM_SCALE)
+    assert np.abs(got["out"][0] - ref).max() <= 2e-3
+
+
+def test_decode_long_256k_sampled_heads():
+    """Full 256K shape in the production launch configuration; oracle on sampled heads."""
+    st = _run(WORKLOADS["long_256k"], 0, [5.0], heads=[(0, 0), (0, 7)])
+    say(f"long_256k keep fractions: {[round(s['keep_frac'], 4) for s in st]}")
+
+
+def test_decode_stress_128k_sampled_heads():
+    """Low-sparsity stress shape (q x 0.1, nothing planted): most blocks kept."""
+    st = _run(WORKLOADS["stress_b4_128k"], 0, [7.0], heads=[(1, 3), (3, 6)])
+    assert all(s["keep_frac"] > 0.5 for s in st)
