@@ -62,8 +62,8 @@ enum ffd_status {
  * block == 64, sink >= 0, local >= 0, sink + local > 0 (the pseudo-max needs
  * at least one support token), max_seq_len a positive multiple of 64,
  * chunk_blocks >= 0 (0 = library choice; otherwise the number of 64-token
- * blocks one work-group scans and refines; it changes only the summation
- * order of the result). */
+ * blocks one work-group scans and refines, capped at 32 for G <= 4 and 16
+ * above; it changes only the summation order of the result). */
 typedef struct ffd_shape {
   int32_t batch;
   int32_t num_q_heads;
@@ -92,7 +92,7 @@ typedef struct ffd_shape {
  *  res     int8   [B][Hkv][nblk][8192]  residual of token t, channel ch at byte
  *              ((ch/16)*64 + t)*16 + ch%16   (two's complement).
  *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t, group g at
- *              element t*4 + g.
+ *              element g*64 + t.
  *  v       fp16   [B][Hkv][max_seq_len][128] values, natural row-major layout.
  *
  * Positions the pack never wrote (beyond the sequence) may hold any bytes:
@@ -105,18 +105,23 @@ typedef struct ffd_cache {
   const void* v;
 } ffd_cache_t;
 
-/* Optional diagnostic outputs of ffd_decode_attn (each pointer may be NULL).
+/* Optional diagnostics of ffd_decode_attn (each pointer may be NULL).
  *  m_tilde       f32 [B][Hq]        pseudo-max per query head
  *  bmax          f32 [B][Hq][nblk]  largest estimated score per block (valid blocks only)
  *  keep          u8  [B][Hkv][nblk] 1 = block kept (valid blocks only)
  *  attend_start  hipEvent_t recorded on the stream right before the fused
- *  attend_stop   scan + refine kernel, and right after it (for timing)       */
+ *  attend_stop   scan + refine kernel, and right after it
+ *  stages        0 = the whole step; otherwise a bitmask of the launches to
+ *                enqueue (1 = pseudo-max, 2 = scan + refine, 4 = merge).  A
+ *                partial call reuses what the previous call left in the same
+ *                workspace (for timing one kernel alone).                     */
 typedef struct ffd_debug {
   float* m_tilde;
   float* bmax;
   uint8_t* keep;
   void* attend_start;
   void* attend_stop;
+  int32_t stages;
 } ffd_debug_t;
 
 /* Bytes of each packed-cache field for `shape` (host call, no GPU work). */
@@ -124,8 +129,9 @@ int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_by
                     size_t* res_bytes, size_t* rscale_bytes);
 
 /* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
- * (host call).  The workspace holds thresholds and per-chunk partials; its
- * contents need no initialisation. */
+ * (host call).  The workspace holds partial pseudo-maxima and per-chunk
+ * attention partials; its contents need no initialisation.  Calls that share
+ * a workspace must be ordered (same stream). */
 int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
 
 /* Work split chosen for `shape`: blocks per work-group and chunks per

@@ -44,7 +44,7 @@ class Cache(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [("m_tilde", ctypes.c_void_p), ("bmax", ctypes.c_void_p), ("keep", ctypes.c_void_p),
-                ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p)]
+                ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p), ("stages", ctypes.c_int32)]
 
 
 _lib = None
@@ -170,7 +170,7 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
     dbg = None
     if debug is not None:
         dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
-                    debug.get("attend_start"), debug.get("attend_stop"))
+                    debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)))
     _check(lib().ffd_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
                                  float(delta), float(sm_scale), _ptr(out), _ptr(workspace),
                                  workspace.numel(), None if dbg is None else ctypes.byref(dbg),

@@ -15,7 +15,6 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTargetGroups = 1024;  // work-groups per launch the automatic split aims for
-constexpr int kMaxChunkBlocks = 64;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -34,26 +33,36 @@ int check_shape(const ffd_shape_t* s) {
 }
 
 struct Plan {
-  int nblk_cap, cb, nchunk;
-  size_t thr_off, ml_off, o_off, total;
+  int nblk_cap, cb, nchunk, npart;
+  size_t pmax_off, ml_off, o_off, total;
 };
 
+// Work split: one work-group per chunk of cb blocks (4 waves, one 16-token tile
+// of every block each).  cb is sized for about kTargetGroups work-groups per
+// launch and bounded by the LDS the per-block estimates of a chunk need.
 Plan make_plan(const ffd_shape_t* s) {
   Plan p;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int cb_max = G <= 4 ? 32 : 16;
   p.nblk_cap = s->max_seq_len / 64;
+  long long cb;
   if (s->chunk_blocks > 0) {
-    p.cb = s->chunk_blocks < p.nblk_cap ? s->chunk_blocks : p.nblk_cap;
+    cb = s->chunk_blocks;
   } else {
     const long long total = (long long)s->batch * s->num_kv_heads * p.nblk_cap;
-    long long cb = (total + kTargetGroups - 1) / kTargetGroups;
-    if (cb < 1) cb = 1;
-    if (cb > kMaxChunkBlocks) cb = kMaxChunkBlocks;
-    p.cb = (int)cb;
+    cb = (total + kTargetGroups - 1) / kTargetGroups;
   }
+  if (cb > cb_max) cb = cb_max;
+  if (cb > p.nblk_cap) cb = p.nblk_cap;
+  if (cb < 1) cb = 1;
+  p.cb = (int)cb;
   p.nchunk = (p.nblk_cap + p.cb - 1) / p.cb;
+  const long long sup = (long long)s->sink + s->local;
+  const long long n_sup = sup < s->max_seq_len ? sup : s->max_seq_len;
+  p.npart = (int)((n_sup + 63) / 64);
   const size_t rows = (size_t)s->batch * s->num_q_heads;
-  p.thr_off = 0;
-  p.ml_off = round_up(rows * sizeof(float), kAlign);
+  p.pmax_off = 0;
+  p.ml_off = round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(float), kAlign);
   p.o_off = p.ml_off + round_up(rows * p.nchunk * 2 * sizeof(float), kAlign);
   p.total = p.o_off + round_up(rows * p.nchunk * 128 * sizeof(float), kAlign);
   return p;
@@ -154,10 +163,12 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
   p.rsc = static_cast<const uint8_t*>(cache->rscale);
   p.v = static_cast<const uint16_t*>(cache->v);
   p.seq_lens = seq_lens;
-  p.thr = reinterpret_cast<float*>(ws + pl.thr_off);
+  p.pmax = reinterpret_cast<float*>(ws + pl.pmax_off);
   p.part_ml = reinterpret_cast<float2*>(ws + pl.ml_off);
   p.part_o = reinterpret_cast<float*>(ws + pl.o_off);
   if (debug) {
+    if (debug->stages < 0 || debug->stages > 7) return FFD_ERR_ARG;
+    p.stages = debug->stages;
     p.dbg_mt = debug->m_tilde;
     p.dbg_bmax = debug->bmax;
     p.dbg_keep = debug->keep;
@@ -172,6 +183,7 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
   p.nblk_cap = pl.nblk_cap;
   p.nchunk = pl.nchunk;
   p.cb = pl.cb;
+  p.npart = pl.npart;
   p.sink = shape->sink;
   p.local = shape->local;
   p.delta = delta;
@@ -198,7 +210,7 @@ int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
   p.seq_lens = seq_lens;
-  p.thr = reinterpret_cast<float*>(ws + pl.thr_off);
+  p.pmax = reinterpret_cast<float*>(ws + pl.pmax_off);
   p.part_ml = reinterpret_cast<float2*>(ws + pl.ml_off);
   p.part_o = reinterpret_cast<float*>(ws + pl.o_off);
   p.out = static_cast<uint16_t*>(out);
@@ -209,6 +221,7 @@ int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k
   p.nblk_cap = pl.nblk_cap;
   p.nchunk = pl.nchunk;
   p.cb = pl.cb;
+  p.npart = pl.npart;
   p.sm_scale = sm_scale;
   return from_hip(ffd::launch_dense_decode(p, static_cast<hipStream_t>(stream)));
 }

@@ -31,7 +31,7 @@ __host__ __device__ inline int sz_off(int t, int g) {
   return ((g * 4 + ((t >> 2) & 3)) * 4 + (t >> 4)) * 16 + (t & 3) * 4;
 }
 __host__ __device__ inline int res_off(int t, int ch) { return ((ch >> 4) * 64 + t) * 16 + (ch & 15); }
-__host__ __device__ inline int rsc_off(int t, int g) { return (t * 4 + g) * 2; }
+__host__ __device__ inline int rsc_off(int t, int g) { return (g * 64 + t) * 2; }
 // bit of channel (32g + 8kq + j) inside its word
 __host__ __device__ inline int code_bit(int g, int j) {
   const int d = j >> 1;

@@ -15,7 +15,7 @@ struct DecodeParams {
   const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
   const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]
   const int32_t* seq_lens; // [B]
-  float* thr;              // [B][Hq]
+  float* pmax;             // [B][npart][Hq] partial pseudo-maxima
   float* part_o;           // [B][Hq][nchunk][128]
   float2* part_ml;         // [B][Hq][nchunk] (m, l)
   float* dbg_mt;           // optional [B][Hq]
@@ -24,7 +24,8 @@ struct DecodeParams {
   uint16_t* out;           // [B][Hq][128] fp16
   hipEvent_t ev_start;     // optional, recorded around the attend kernel
   hipEvent_t ev_stop;
-  int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, sink, local;
+  int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge
+  int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
   float delta, sm_scale;
 };
 

@@ -45,7 +45,7 @@ def _res_map():
 _WORD, _BIT = _code_maps()
 _SZ = _sz_map()
 _RES = _res_map()
-_RSC = (np.arange(64)[:, None] * 4 + np.arange(4)[None, :])
+_RSC = (np.arange(4)[None, :] * 64 + np.arange(64)[:, None])      # [t][g] -> element g*64 + t
 
 
 def decode_cache(codes: np.ndarray, sz: np.ndarray, res: np.ndarray, rscale: np.ndarray,

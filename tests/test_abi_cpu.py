@@ -122,17 +122,21 @@ def test_cache_and_workspace_sizes():
     cb, nch = ffd.plan(s)
     assert nch == math.ceil(512 / cb)
     rows = 2 * 28
-    need = rows * 4 + rows * nch * 8 + rows * nch * 128 * 4
+    npart = math.ceil((64 + 256) / 64)
+    need = rows * npart * 4 + rows * nch * 8 + rows * nch * 128 * 4
     assert need <= ffd.workspace_bytes(s) <= need + 3 * 256
 
 
-@pytest.mark.parametrize("B,Hkv,L,expect", [(1, 8, 16384, 2), (1, 8, 262144, 32), (16, 4, 32768, 32),
-                                            (1, 1, 4096, 1), (4, 8, 131072, 64)])
-def test_automatic_split(B, Hkv, L, expect):
-    cb, nch = ffd.plan(ffd.make_shape(B, Hkv, Hkv, L))
+@pytest.mark.parametrize("B,Hq,Hkv,L,expect", [(1, 32, 8, 16384, 2), (1, 32, 8, 262144, 32),
+                                               (16, 28, 4, 32768, 16), (1, 4, 1, 4096, 1),
+                                               (4, 32, 8, 131072, 32), (1, 1, 1, 64, 1)])
+def test_automatic_split(B, Hq, Hkv, L, expect):
+    """About 1024 work-groups per launch; at most 32 blocks per chunk (16 when G > 4)."""
+    cb, nch = ffd.plan(ffd.make_shape(B, Hq, Hkv, L))
     assert cb == expect and nch == math.ceil(L // 64 / cb)
-    cb, nch = ffd.plan(ffd.make_shape(B, Hkv, Hkv, L, chunk_blocks=10 ** 6))
-    assert cb == L // 64 and nch == 1
+    cb, nch = ffd.plan(ffd.make_shape(B, Hq, Hkv, L, chunk_blocks=10 ** 6))
+    cap = 32 if Hq // Hkv <= 4 else 16
+    assert cb == min(cap, L // 64) and nch == math.ceil(L // 64 / cb)
 
 
 def test_layout_maps_are_bijective():
