@@ -7,13 +7,15 @@ in HBM.  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
 delta=5), plus the 256K long-context shape with the in-house dense
 flash-decode kernel timed beside it.
 
-Timing: W untimed warm-up steps, then exactly K timed steps bracketed by
-torch.cuda.synchronize(); per-layer caches are rotated (each step reads a
-different copy) so that the bytes touched between two visits of the same copy
-exceed the 256 MB last-level cache.  The fused scan + refine + merge kernel is
-then timed alone: K back-to-back launches of it between two HIP events that
-the library records on the launch stream; the mean launch duration is the
-roofline denominator.
+Timing: the decode step is captured in a HIP graph, as the pages do with
+CUDA graphs to remove CPU launch overhead: W untimed warm-up steps, then one
+graph of exactly K steps replayed between two events and bracketed by
+torch.cuda.synchronize().  Per-layer caches are rotated (step i reads copy
+i mod R) so that the bytes touched between two visits of the same copy exceed
+the 256 MB last-level cache.  The fused scan + refine kernel is then timed
+alone: a graph of K back-to-back launches of it (stage mask 2) on the same
+stream; its mean launch duration is the roofline denominator.  Eager
+(uncaptured) launches are timed too and reported as eager_us_per_step.
 
 Roofline: achieved = algorithmic bytes of the fused kernel per launch (48 B per
 token-head scanned + 392 B per kept token-head refined) / its mean duration,
@@ -22,7 +24,6 @@ against the 8 TB/s HBM3E peak.
 from __future__ import annotations
 
 import argparse
-import ctypes
 import json
 import math
 import os
@@ -45,29 +46,25 @@ ROTATE_TARGET = 1.5e9
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
 
-class HipEvents:
-    """Minimal hipEvent API through ctypes (events recorded by libffd itself)."""
+def graph_of(calls, torch):
+    """Capture a list of zero-argument launch callables into one HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self):
-        self.h = ctypes.CDLL("libamdhip64.so")
-        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
-    def create(self) -> int:
-        e = ctypes.c_void_p()
-        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
-        return e.value
-
-    def elapsed_ms(self, a: int, b: int) -> float:
-        assert self.h.hipEventSynchronize(ctypes.c_void_p(b)) == 0
-        ms = ctypes.c_float()
-        assert self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
-        return ms.value
-
-    def destroy(self, e: int) -> None:
-        self.h.hipEventDestroy(ctypes.c_void_p(e))
+def timed_replay(g, torch) -> float:
+    """Replay a captured graph between two events; returns milliseconds."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
 def log(msg):
@@ -123,39 +120,39 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
         layers.append(cc)
     log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
 
+    def step(i, stages=0):
+        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
+                        debug={"stages": stages} if stages else None)
+
+    # eager launches (host-bound for short contexts), for reference
     for i in range(warmup):
-        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws)
+        step(i)
     torch.cuda.synchronize()
-    # whole steps: pseudo-max + fused scan/refine/merge, back to back
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    eager_us = t0.elapsed_time(t1) * 1e3 / steps
+    # the decode step as the pages run it: captured in a graph (K steps over the
+    # rotated layers per replay); W warm-up steps replayed first
+    g_warm, g_steps, g_attend = graph_of([lambda i=i: step(i) for i in range(warmup)], torch), \
+        graph_of([lambda i=i: step(i) for i in range(steps)], torch), \
+        graph_of([lambda i=i: step(i, stages=2) for i in range(steps)], torch)
+    g_warm.replay()
+    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(steps):
-        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws)
-    t_stop.record()
-    torch.cuda.synchronize()
+    total_ms = timed_replay(g_steps, torch)
     wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_stop)
-    # the fused kernel alone: `steps` back-to-back launches between two HIP events
-    # recorded by the library on the launch stream (pseudo-max state from above)
-    ev = HipEvents()
-    e0, e1 = ev.create(), ev.create()
-    for i in range(steps):
-        dbg = {"stages": 2}
-        if i == 0:
-            dbg["attend_start"] = e0
-        if i == steps - 1:
-            dbg["attend_stop"] = e1
-        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws, debug=dbg)
-    attend_total_ms = ev.elapsed_ms(e0, e1)
-    ev.destroy(e0)
-    ev.destroy(e1)
+    g_attend.replay()
+    attend_total_ms = timed_replay(g_attend, torch)
     us_step = total_ms * 1e3 / steps
     attend_us = attend_total_ms * 1e3 / steps
     return {
         "us_per_step": us_step,
         "wall_us_per_step": wall * 1e6 / steps,
+        "eager_us_per_step": eager_us,
         "attend_us_mean": attend_us,
         "keep_fraction": keep_frac,
         "attend_bytes": attend_bytes,
@@ -175,16 +172,13 @@ def measure_dense(w, steps, warmup, d, torch, sm_scale):
     R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
     ks = [d["k"]] + [d["k"].clone() for _ in range(R - 1)]
     vs = [d["v"]] + [d["v"].clone() for _ in range(R - 1)]
-    for i in range(warmup):
+    def step(i):
         ffd.dense_decode_attn(shape, d["q"], ks[i % R], vs[i % R], d["seq_lens"], sm_scale, out, ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        ffd.dense_decode_attn(shape, d["q"], ks[i % R], vs[i % R], d["seq_lens"], sm_scale, out, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+
+    g_warm = graph_of([lambda i=i: step(i) for i in range(warmup)], torch)
+    g_steps = graph_of([lambda i=i: step(i) for i in range(steps)], torch)
+    g_warm.replay()
+    us = timed_replay(g_steps, torch) * 1e3 / steps
     byts = DENSE_BYTES * int(d["seq_lens"].sum().item()) * w.kv_heads
     del ks, vs
     return {"us_per_step": us, "bytes": byts, "gbps": byts / us / 1e3, "layers_rotated": R}

@@ -14,7 +14,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTargetGroups = 1024;  // work-groups per launch the automatic split aims for
+constexpr int kTargetGroups = 2048;  // work-groups per launch the automatic split aims for
+constexpr int kSmallGroups = 256;    // ... and at least this many blocks per 4-block group on short caches
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -49,17 +50,26 @@ Plan make_plan(const ffd_shape_t* s) {
   if (s->chunk_blocks > 0) {
     cb = s->chunk_blocks;
   } else {
+    // about kTargetGroups work-groups on long caches; short caches take up to
+    // 4 blocks per work-group so that one wave of work-groups covers them
     const long long total = (long long)s->batch * s->num_kv_heads * p.nblk_cap;
     cb = (total + kTargetGroups - 1) / kTargetGroups;
+    if (cb < 4) {
+      const long long small = (total + kSmallGroups - 1) / kSmallGroups;
+      cb = small < 4 ? small : 4;
+    }
   }
   if (cb > cb_max) cb = cb_max;
   if (cb > p.nblk_cap) cb = p.nblk_cap;
   if (cb < 1) cb = 1;
   p.cb = (int)cb;
   p.nchunk = (p.nblk_cap + p.cb - 1) / p.cb;
-  const long long sup = (long long)s->sink + s->local;
-  const long long n_sup = sup < s->max_seq_len ? sup : s->max_seq_len;
-  p.npart = (int)((n_sup + 63) / 64);
+  // pseudo-max work-groups: one per block that can hold support tokens (sink
+  // blocks, then the blocks spanned by the local window, at most one extra)
+  const long long sink_blocks = ((long long)(s->sink < s->max_seq_len ? s->sink : s->max_seq_len) + 63) / 64;
+  const long long local_blocks = s->local > 0 ? ((long long)s->local + 63) / 64 + 1 : 0;
+  const long long np = sink_blocks + local_blocks;
+  p.npart = (int)(np < p.nblk_cap ? np : p.nblk_cap);
   const size_t rows = (size_t)s->batch * s->num_q_heads;
   p.pmax_off = 0;
   p.ml_off = round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(float), kAlign);

@@ -1,6 +1,6 @@
-// FFD decode attention, one step: pseudo-max, then one fused kernel that scans
-// the 2-bit thumbnail, refines the kept blocks and merges the partials; plus the
-// dense flash-decode baseline built from the same pieces.
+// FFD decode attention, one step: pseudo-max, a fused kernel that scans the 2-bit
+// thumbnail and refines the kept blocks, and a log-sum-exp merge; plus the dense
+// flash-decode baseline built from the same pieces.
 //
 // Page: "Faster Than Flash" (gist.science summary of arXiv 2609.00097).
 //   Method 2 (Top-delta): keep when s >= m~ - delta, m~ from sink + local tokens.
@@ -12,6 +12,16 @@
 //            scores kept on chip)                          -> attend_kernel phase B
 //   log-sum-exp merge of the per-chunk partials            -> merge_kernel
 //
+// Scores are computed per 16-token tile with MFMA 16x16x32 f16, tokens on the
+// rows.  The B operand holds q with column n = 4*h + g carrying head h
+// restricted to 32-channel group g (zero elsewhere), so one accumulator
+// collects per-(head, group) dot products whose fp32 epilogue applies that
+// token-group's scale; a quad sum over g finishes the dot product.
+//   thumbnail: A = 1 + c/4 (exact fp16), accumulator starts at -sum_g(q):
+//              C = (q_g . c_g)/4;  est = 4*scale*C + zero*sum_g(q)
+//   residual:  A = 384 + e (exact fp16), accumulator starts at -384*sum_g(q):
+//              C = q_g . e_g;      exact = est + rscale*C
+//
 // Work decomposition of attend/dense: one work-group (4 wave64) per chunk of `cb`
 // 64-token blocks of one (sequence, KV head).  Wave w owns token tile
 // [16w, 16w+16) of every block of the chunk, so the four waves do identical work
@@ -21,6 +31,8 @@
 #include "ffd_launch.h"
 
 namespace ffd {
+
+constexpr int kWaves = 4;
 
 __device__ inline int clamp_len(const DecodeParams& p, int b) {
   const int L = p.seq_lens[b];
@@ -34,109 +46,22 @@ __device__ inline float quad_sum(float v) {
   return v;
 }
 
-// ---------------------------------------------------------------------------
-// Stage 1: pseudo-max over support tokens [0, min(S,L)) U [max(0,L-W), L).
-// Grid (npart, Hkv, B), 256 threads; work-group `part` takes support tokens
-// [64*part, 64*part + 64); thread = (token, group).  Exact score of a token:
-// sum over groups of scale*(q.c) + zero*sum(q) + rscale*(q.e) with K-hat =
-// zero + c*scale + e*rscale.  Writes the part's maximum per query head; the
-// attend kernel takes the maximum over parts.
-// ---------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
-  __shared__ float qs[G][kHeadDim];
-  __shared__ float qsum[G][kGroups];
-  __shared__ float red[4][G];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const size_t head = (size_t)b * p.Hkv + hkv;
-  const int L = clamp_len(p, b);
-  const int qh0 = hkv * G;
-  for (int i = tid; i < G * kHeadDim; i += 256)
-    qs[i >> 7][i & 127] = h2f(p.q[((size_t)b * p.Hq + qh0 + (i >> 7)) * kHeadDim + (i & 127)]);
-  __syncthreads();
-  if (tid < G * kGroups) {
-    const int h = tid >> 2, g = tid & 3;
-    float s = 0.f;
-    for (int k = 0; k < kGroup; ++k) s += qs[h][32 * g + k];
-    qsum[h][g] = s;
-  }
-  __syncthreads();
-
-  const int n_s = min(p.sink, L);
-  const int lo = max(n_s, L - p.local);
-  const int n = n_s + (L - lo);
-  const int j = part * 64 + (tid >> 2);
-  const int g = tid & 3;
-  const bool valid = j < n;
-  const int t = !valid ? 0 : (j < n_s ? j : lo + (j - n_s));
-  const int tb = t & 63;
-  const size_t bi = head * p.nblk_cap + (t >> 6);
-  const uint8_t* cb = p.codes + bi * kCodesBytes;
-  const uint32_t zw = *reinterpret_cast<const uint32_t*>(p.sz + bi * kSzBytes + sz_off(tb, g));
-  const float s = lo_h(zw), z = hi_h(zw);
-  const float s8 = h2f(*reinterpret_cast<const uint16_t*>(p.rsc + bi * kRscBytes + rsc_off(tb, g)));
-  const int8_t* rb = p.res + bi * kResBytes;
-  float A[G], E[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { A[h] = 0.f; E[h] = 0.f; }
-#pragma unroll 1
-  for (int kq = 0; kq < 4; ++kq) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(cb + codes_word_off(tb, kq, g >> 1));
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float c = (float)((w >> code_bit(g, jj)) & 3u);
-#pragma unroll
-      for (int h = 0; h < G; ++h) A[h] = fmaf(qs[h][32 * g + 8 * kq + jj], c, A[h]);
-    }
-  }
-#pragma unroll 1
-  for (int half = 0; half < 2; ++half) {
-    const uint4 rv = *reinterpret_cast<const uint4*>(rb + res_off(tb, 32 * g + 16 * half));
-    const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = (float)(int8_t)((rw[i >> 2] >> (8 * (i & 3))) & 0xffu);
-#pragma unroll
-      for (int h = 0; h < G; ++h) E[h] = fmaf(qs[h][32 * g + 16 * half + i], e, E[h]);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v = quad_sum(s * A[h] + z * qsum[h][g] + s8 * E[h]) * p.sm_scale;
-    v = valid ? v : -INFINITY;
-    v = wave_max(v);
-    if (lane == 0) red[wave][h] = v;
-  }
-  __syncthreads();
-  if (tid < G) {
-    const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-    p.pmax[((size_t)b * p.npart + part) * p.Hq + qh0 + tid] = m;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// pieces shared by the attend and dense kernels
-// ---------------------------------------------------------------------------
-constexpr int kWaves = 4;
-
 // 2-bit code word -> MFMA A fragment of 8 fp16 values 1 + c/4 (channels j = 0..7)
-__device__ inline h8 unpack_even(uint32_t w) {
-  const uint32_t M = 0x03000300u, BIAS = 0x3C003C00u;
+constexpr uint32_t kCodeMask = 0x03000300u, kOneHalf2 = 0x3C003C00u;
+__device__ inline h8 unpack_even(uint32_t w, uint32_t one) {
   uint4 d;
-  d.x = (w & M) | BIAS;
-  d.y = ((w >> 2) & M) | BIAS;
-  d.z = ((w >> 4) & M) | BIAS;
-  d.w = ((w >> 6) & M) | BIAS;
+  d.x = and_or(w, kCodeMask, one);
+  d.y = and_or(w >> 2, kCodeMask, one);
+  d.z = and_or(w >> 4, kCodeMask, one);
+  d.w = and_or(w >> 6, kCodeMask, one);
   return __builtin_bit_cast(h8, d);
 }
-__device__ inline h8 unpack_odd(uint32_t w) {
-  const uint32_t M = 0x03000300u, BIAS = 0x3C003C00u;
+__device__ inline h8 unpack_odd(uint32_t w, uint32_t one) {
   uint4 d;
-  d.x = ((w << 8) & M) | BIAS;
-  d.y = ((w << 6) & M) | BIAS;
-  d.z = ((w << 4) & M) | BIAS;
-  d.w = ((w << 2) & M) | BIAS;
+  d.x = and_or(w << 8, kCodeMask, one);
+  d.y = and_or(w << 6, kCodeMask, one);
+  d.z = and_or(w << 4, kCodeMask, one);
+  d.w = and_or(w << 2, kCodeMask, one);
   return __builtin_bit_cast(h8, d);
 }
 // 8 int8 residuals -> MFMA A fragment of fp16 values 384 + e (exact)
@@ -153,9 +78,187 @@ __device__ inline h8 unpack_res(uint2 r) {
   return __builtin_bit_cast(h8, d);
 }
 
+// ---------------------------------------------------------------------------
+// q operands of the tile MFMAs.  Lane roles: col = lane & 15 (C column,
+// head hc = col >> 2 of the 4-head column tile, group gc = col & 3),
+// ks = lane >> 4 (A/B k-slice, C row group).
+// ---------------------------------------------------------------------------
+template <int G>
+struct QFrags {
+  static constexpr int NT = (G + 3) / 4;  // 16-column tiles (4 heads x 4 groups each)
+  h8 B[NT][kGroups];
+  float c_est[NT], c_res[NT], qq[NT];
+
+  // q2: q as fp16 pairs [G][64]; qg: per-(head, group) sums of q
+  __device__ void build(const h2 (*q2)[64], const float (*qg)[kGroups], int lane) {
+    const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int h = 4 * nt + hc;
+      const bool live = h < G;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        h8 f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          h2 pr = {(_Float16)0.f, (_Float16)0.f};
+          if (live && g == gc) pr = q2[h][16 * g + 4 * ks + d];
+          f[2 * d] = pr.x;
+          f[2 * d + 1] = pr.y;
+        }
+        B[nt][g] = f;
+      }
+      const float Q = live ? qg[h][gc] : 0.f;
+      c_est[nt] = -Q;
+      c_res[nt] = -384.f * Q;
+      qq[nt] = 0.25f * Q;
+    }
+  }
+
+  // estimated scores of the lane's 4 C rows divided by 4*sm_scale; cw = codes
+  // words (groups 0,1 | 2,3) of the lane's A row, zw = (scale, zero) of the
+  // lane's 4 C rows for group gc
+  __device__ void estimate(uint2 cw, uint4 zw, float (&e)[NT][4]) const {
+    const uint32_t one = kOneHalf2;
+    const h8 a0 = unpack_even(cw.x, one), a1 = unpack_odd(cw.x, one);
+    const h8 a2 = unpack_even(cw.y, one), a3 = unpack_odd(cw.y, one);
+    const uint32_t zs[4] = {zw.x, zw.y, zw.z, zw.w};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f4 c = {c_est[nt], c_est[nt], c_est[nt], c_est[nt]};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, B[nt][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B[nt][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B[nt][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, B[nt][3], c, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[nt][i] = quad_sum(fmaf(lo_h(zs[i]), c[i], fmaf(hi_h(zs[i]), qq[nt], 0.f)));
+    }
+  }
+
+  // residual term sm_scale * sum_g rscale_g * (q_g . e_g) of the lane's 4 C
+  // rows; R[g] = residual bytes of the lane's A row for group g, S8 = rscale
+  // of the lane's 4 C rows for group gc
+  __device__ void residual(const uint2 (&R)[kGroups], uint2 S8, float sm_scale, float (&r)[NT][4]) const {
+    const h8 a0 = unpack_res(R[0]), a1 = unpack_res(R[1]), a2 = unpack_res(R[2]), a3 = unpack_res(R[3]);
+    const float s8[4] = {lo_h(S8.x), hi_h(S8.x), lo_h(S8.y), hi_h(S8.y)};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f4 c = {c_res[nt], c_res[nt], c_res[nt], c_res[nt]};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, B[nt][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, B[nt][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B[nt][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, B[nt][3], c, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[nt][i] = quad_sum(s8[i] * c[i]) * sm_scale;
+    }
+  }
+};
+
+// per-lane byte offsets of one tile's packed data inside a block
+struct TileOffsets {
+  int codes, sz, res, rsc;
+  __device__ TileOffsets(int wave, int lane) {
+    const int col = lane & 15, gc = col & 3, ks = lane >> 4;
+    codes = ((col * 4 + ks) * 4 + wave) * 8;                                // A row token 16w+col, slice ks
+    sz = ((gc * 4 + ks) * 4 + wave) * 16;                                   // C rows 16w+4ks.., group gc
+    res = (((ks >> 1) * 64) + 16 * wave + col) * 16 + 8 * (ks & 1);         // + group * 2048
+    rsc = (gc * 64 + 16 * wave + 4 * ks) * 2;                               // C rows, group gc
+  }
+};
+
+__device__ inline void load_residual(const int8_t* rb, const uint8_t* sb, const TileOffsets& to,
+                                     uint2 (&R)[kGroups], uint2& S8) {
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) R[g] = *reinterpret_cast<const uint2*>(rb + to.res + g * 2048);
+  S8 = *reinterpret_cast<const uint2*>(sb + to.rsc);
+}
+
+// q of the group's heads into LDS as fp16 pairs, and per-(head, group) sums
+template <int G>
+__device__ inline void stage_q(const DecodeParams& p, int b, int qh0, int tid, h2 (*q2)[64]) {
+  for (int i = tid; i < G * 64; i += 256)
+    q2[i >> 6][i & 63] = __builtin_bit_cast(
+        h2, *reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + qh0 + (i >> 6)) * kHeadDim + 2 * (i & 63)));
+}
+template <int G>
+__device__ inline void group_sums(const h2 (*q2)[64], float (*qg)[kGroups], int tid) {
+  if (tid < G * kGroups) {
+    const int h = tid >> 2, g = tid & 3;
+    float s = 0.f;
+    for (int k = 0; k < 16; ++k) { const h2 v = q2[h][16 * g + k]; s += (float)v.x + (float)v.y; }
+    qg[h][g] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1: pseudo-max over support tokens [0, min(S,L)) U [max(0,L-W), L),
+// exact scores with K-hat.  Grid (npart, Hkv, B), 4 waves: work-group `part`
+// takes one block holding support tokens (sink blocks first, then local
+// blocks not already covered), wave w its 16-token tile.  Writes the part's
+// maximum per query head (-inf for parts without a block); the attend kernel
+// takes the maximum over parts.
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
+  constexpr int NT = QFrags<G>::NT;
+  __shared__ h2 q2[G][64];
+  __shared__ float qg[G][kGroups];
+  __shared__ float red[kWaves][G];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const size_t head = (size_t)b * p.Hkv + hkv;
+  const int qh0 = hkv * G;
+  stage_q<G>(p, b, qh0, tid, q2);
+  const int L = clamp_len(p, b);
+  const int nblk = (L + 63) >> 6;
+  const int s_end = min(p.sink, L);
+  const int l_beg = p.local > 0 ? max(0, L - p.local) : L;
+  const int n_sink_blk = (s_end + 63) >> 6;
+  const int first_local = max(l_beg >> 6, n_sink_blk);
+  const int blk = part < n_sink_blk ? part : first_local + (part - n_sink_blk);
+  const bool live = blk < nblk && (part < n_sink_blk || l_beg < L);
+  const int blk_c = live ? blk : 0;
+  const size_t bi = head * p.nblk_cap + blk_c;
+  const TileOffsets to(wave, lane);
+  const uint2 cw = *reinterpret_cast<const uint2*>(p.codes + bi * kCodesBytes + to.codes);
+  const uint4 zw = *reinterpret_cast<const uint4*>(p.sz + bi * kSzBytes + to.sz);
+  uint2 R[kGroups], S8;
+  load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, R, S8);
+  __syncthreads();
+  group_sums<G>(q2, qg, tid);
+  __syncthreads();
+  QFrags<G> qf;
+  qf.build(q2, qg, lane);
+  float e[NT][4], r[NT][4];
+  qf.estimate(cw, zw, e);
+  qf.residual(R, S8, p.sm_scale, r);
+  const float scale4 = 4.f * p.sm_scale;
+  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = blk_c * 64 + 16 * wave + 4 * ks + i;
+      const bool sup = live && t < L && (t < s_end || t >= l_beg);
+      mx = fmaxf(mx, sup ? fmaf(e[nt][i], scale4, r[nt][i]) : -INFINITY);
+    }
+    mx = rows_max(mx);
+    const int h = 4 * nt + hc;
+    if (ks == 0 && gc == 0 && h < G) red[wave][h] = mx;
+  }
+  __syncthreads();
+  if (tid < G) {
+    const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    p.pmax[((size_t)b * p.npart + part) * p.Hq + qh0 + tid] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Per-wave online-softmax state.  Scores arrive in MFMA C layout: lane
 // (ks = lane>>4, column) holds rows 4ks..4ks+3 of a 16-token tile for the head
 // of its column.  NS score sets per lane (FFD: one per 16-column tile).
+// ---------------------------------------------------------------------------
 template <int G, int NS>
 struct WaveSoftmax {
   float m[NS];
@@ -170,11 +273,9 @@ struct WaveSoftmax {
       for (int k = 0; k < 8; ++k) acc[h][k] = 0.f;
   }
   // fold one score set: returns alpha = exp(m_old - m_new) of the lane's head
-  __device__ float fold(int n, float (&s)[4], float* pw_rows /* [16][pg] */, int pg, int head, bool writer,
-                        int ks) {
-    float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    tm = fmaxf(tm, xor_lane(tm, 16));
-    tm = fmaxf(tm, xor_lane(tm, 32));
+  __device__ float fold(int n, const float (&s)[4], float* pw_rows /* [16][pg] */, int pg, int head,
+                        bool writer, int ks) {
+    const float tm = rows_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     const float mn = fmaxf(m[n], tm);
     const bool live = mn > -INFINITY;
     const float alpha = live ? exp2f((m[n] - mn) * kLog2e) : 1.f;
@@ -185,8 +286,7 @@ struct WaveSoftmax {
       ps += pi;
       if (writer) pw_rows[(4 * ks + i) * pg + head] = pi;
     }
-    ps += xor_lane(ps, 16);
-    ps += xor_lane(ps, 32);
+    ps = rows_sum(ps);
     l[n] = l[n] * alpha + ps;
     m[n] = mn;
     return alpha;
@@ -195,10 +295,15 @@ struct WaveSoftmax {
   template <int PG>
   __device__ void pv(const float (&alpha)[G], const uint4 (&Vr)[4], const float* pw_rows, int lane,
                      int n_rows_valid) {
+    bool rescale = false;  // alpha is wave-uniform: skip the rescale when no head's max moved
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) rescale = rescale || (alpha[h] != 1.f);
+    if (rescale) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[h][k] *= alpha[h];
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[h][k] *= alpha[h];
+    }
     const int tp = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -242,10 +347,7 @@ __device__ void finish_chunk(const DecodeParams& p, CombineLds<G>& cl, float (&a
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      float a = acc[h][k];
-      a += xor_lane(a, 16);
-      a += xor_lane(a, 32);
-      acc[h][k] = a;
+      acc[h][k] = rows_sum(acc[h][k]);
     }
   if (lane < 16) {
 #pragma unroll
@@ -284,24 +386,17 @@ __device__ void finish_chunk(const DecodeParams& p, CombineLds<G>& cl, float (&a
 }
 
 // ---------------------------------------------------------------------------
-// Stages 2 + 3.
-//
-// Scan (phase A, MFMA 16x16x32 f16): per 16-token tile, A = codes as fp16
-// (1 + c/4), tokens on rows; B = q with column n = 4*h + g holding head h
-// restricted to group g (zero elsewhere), so one accumulator collects
-// C[t][(h,g)] = sum_{k in g} (1 + c_k/4) q_hk; starting it at -sum_{k in g} q_hk
-// leaves (q_g . c_g)/4.  The fp32 epilogue scales by the group's scale and adds
-// zero*sum(q); a quad sum over g gives the estimate.  Block max per head against
-// the head's threshold decides the block (union over the GQA group).
-//
-// Refine (phase B): the residual term uses the same MFMA shape with A = 384 + e
-// (exact in fp16) and accumulator start -384*sum(q); exact score = estimate
-// (kept in LDS from phase A) + rscale * (q . e); online softmax in the MFMA
-// output layout; P.V on VALU with lanes over channels.
+// Stages 2 + 3 for one chunk of blocks.
+//   phase A: every wave estimates its tile of every block of the chunk (loads
+//            double-buffered in batches of 4 blocks); estimates stay in LDS
+//   decide:  block kept if it holds a support token, or some head's block
+//            max of the estimate reaches that head's threshold
+//   phase B: every wave refines its tile of every kept block (next kept
+//            block prefetched), online softmax, P.V
 // ---------------------------------------------------------------------------
 template <int G>
 struct AttendCfg {
-  static constexpr int NT = (G + 3) / 4;
+  static constexpr int NT = QFrags<G>::NT;
   static constexpr int PG = (G + 3) & ~3;
   static constexpr int CBMAX = (G <= 4) ? 32 : 16;
 };
@@ -311,18 +406,32 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   constexpr int NT = AttendCfg<G>::NT, PG = AttendCfg<G>::PG, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int L = clamp_len(p, b);
-  const int nblk = (L + 63) >> 6;
   const int blk0 = chunk * p.cb;
-  if (blk0 >= nblk) return;
-  const int nbl = min(p.cb, nblk - blk0);
+  const int nbl_cap = min(p.cb, p.nblk_cap - blk0);
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
+  const TileOffsets to(wave, lane);
+  const size_t bi0 = head * p.nblk_cap + blk0;
+  const uint8_t* cbase = p.codes + bi0 * kCodesBytes + to.codes;
+  const uint8_t* zbase = p.sz + bi0 * kSzBytes + to.sz;
+
+  // first thumbnail batch: independent of the sequence length and of q
+  uint2 cwA[4], cwB[4];
+  uint4 zwA[4], zwB[4];
+  auto load_batch = [&](int j0, uint2 (&cw)[4], uint4 (&zw)[4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int jj = min(j0 + v, nbl_cap - 1);
+      cw[v] = *reinterpret_cast<const uint2*>(cbase + (size_t)jj * kCodesBytes);
+      zw[v] = *reinterpret_cast<const uint4*>(zbase + (size_t)jj * kSzBytes);
+    }
+  };
+  load_batch(0, cwA, zwA);
 
   __shared__ h2 q2[G][64];
   __shared__ float qg[G][kGroups];
   __shared__ float thr_s[G];
-  __shared__ float tmax[CBMAX][kWaves][G];
+  __shared__ float tmax[CBMAX][4 * kWaves][G];  // per (block, wave, row group) maxima
   __shared__ int klist[CBMAX];
   __shared__ int nkeep;
   __shared__ float pw[kWaves][16 * PG];
@@ -331,100 +440,62 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     CombineLds<G> cl;
   } u;
 
-  for (int i = tid; i < G * 64; i += 256)
-    q2[i >> 6][i & 63] = __builtin_bit_cast(
-        h2, *reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + qh0 + (i >> 6)) * kHeadDim + 2 * (i & 63)));
+  stage_q<G>(p, b, qh0, tid, q2);
+  float mt = -INFINITY;  // pseudo-max of head `tid`: max over the parts (loads issued with the others)
+  if (tid < G)
+    for (int pp = 0; pp < p.npart; ++pp) mt = fmaxf(mt, p.pmax[((size_t)b * p.npart + pp) * p.Hq + qh0 + tid]);
+  const int L = clamp_len(p, b);
+  const int nblk = (L + 63) >> 6;
+  if (blk0 >= nblk) return;
+  const int nbl = min(p.cb, nblk - blk0);
   if (tid < G) {
-    float m = -INFINITY;
-    for (int pp = 0; pp < p.npart; ++pp) m = fmaxf(m, p.pmax[((size_t)b * p.npart + pp) * p.Hq + qh0 + tid]);
-    thr_s[tid] = m - p.delta;
-    if (chunk == 0 && p.dbg_mt) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = m;
+    thr_s[tid] = mt - p.delta;
+    if (chunk == 0 && p.dbg_mt) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = mt;
   }
   __syncthreads();
-  if (tid < G * kGroups) {
-    const int h = tid >> 2, g = tid & 3;
-    float s = 0.f;
-    for (int k = 0; k < 16; ++k) { const h2 v = q2[h][16 * g + k]; s += (float)v.x + (float)v.y; }
-    qg[h][g] = s;
-  }
+  group_sums<G>(q2, qg, tid);
   __syncthreads();
-
-  // MFMA lane roles: A row / C column = lane & 15, k-slice / C row group = lane >> 4
-  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
-  h8 Bf[NT][kGroups];
-  float c_est[NT], c_res[NT], qq[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int h = 4 * nt + hc;
-    const bool live = h < G;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      h8 f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        h2 pr = {(_Float16)0.f, (_Float16)0.f};
-        if (live && g == gc) pr = q2[h][16 * g + 4 * ks + d];
-        f[2 * d] = pr.x;
-        f[2 * d + 1] = pr.y;
-      }
-      Bf[nt][g] = f;
-    }
-    const float Q = live ? qg[h][gc] : 0.f;
-    c_est[nt] = -Q;
-    c_res[nt] = -384.f * Q;
-    qq[nt] = 0.25f * Q;
-  }
+  QFrags<G> qf;
+  qf.build(q2, qg, lane);
   const float scale4 = 4.f * p.sm_scale;
+  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
 
-  // ---- phase A: scan tile `wave` of every block of the chunk ----
-  {
-    const size_t bi0 = head * p.nblk_cap + blk0;
-    const uint8_t* cbase = p.codes + bi0 * kCodesBytes + ((col * 4 + ks) * 4 + wave) * 8;
-    const uint8_t* zbase = p.sz + bi0 * kSzBytes + ((gc * 4 + ks) * 4 + wave) * 16;
-    for (int j0 = 0; j0 < nbl; j0 += 4) {
-      uint2 cw[4];
-      uint4 zw[4];
+  // ---- phase A: estimate tile `wave` of every block of the chunk ----
+  // estimates are kept divided by 4*sm_scale; rows past the sequence end (only
+  // in the last block) are set to -inf
+  auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint4 (&zw)[4]) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int jj = min(j0 + v, nbl - 1);
-        cw[v] = *reinterpret_cast<const uint2*>(cbase + (size_t)jj * kCodesBytes);
-        zw[v] = *reinterpret_cast<const uint4*>(zbase + (size_t)jj * kSzBytes);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int j = j0 + v;
-        if (j < nbl) {
-          const h8 a0 = unpack_even(cw[v].x), a1 = unpack_odd(cw[v].x);
-          const h8 a2 = unpack_even(cw[v].y), a3 = unpack_odd(cw[v].y);
-          const uint32_t zs[4] = {zw[v].x, zw[v].y, zw[v].z, zw[v].w};
+    for (int v = 0; v < 4; ++v) {
+      const int j = j0 + v;
+      if (j < nbl) {
+        float e[NT][4];
+        qf.estimate(cw[v], zw[v], e);
+        if ((blk0 + j + 1) * 64 > L) {
           const int row0 = (blk0 + j) * 64 + 16 * wave + 4 * ks;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            f4 c = {c_est[nt], c_est[nt], c_est[nt], c_est[nt]};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bf[nt][0], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bf[nt][1], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, Bf[nt][2], c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, Bf[nt][3], c, 0, 0, 0);
-            float e4[4];
-            float mx = -INFINITY;
+          for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float v4 = quad_sum(fmaf(lo_h(zs[i]), c[i], hi_h(zs[i]) * qq[nt]));
-              v4 = (row0 + i < L) ? v4 * scale4 : -INFINITY;
-              e4[i] = v4;
-              mx = fmaxf(mx, v4);
-            }
-            mx = fmaxf(mx, xor_lane(mx, 16));
-            mx = fmaxf(mx, xor_lane(mx, 32));
-            const int h = 4 * nt + hc;
-            if (gc == 0 && h < G) {
-              *reinterpret_cast<float4*>(&u.est[j][wave][h][4 * ks]) = make_float4(e4[0], e4[1], e4[2], e4[3]);
-              if (ks == 0) tmax[j][wave][h] = mx;
-            }
+            for (int i = 0; i < 4; ++i) e[nt][i] = (row0 + i < L) ? e[nt][i] : -INFINITY;
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float mx = fmaxf(fmaxf(e[nt][0], e[nt][1]), fmaxf(e[nt][2], e[nt][3]));
+          const int h = 4 * nt + hc;
+          if (gc == 0 && h < G) {
+            *reinterpret_cast<float4*>(&u.est[j][wave][h][4 * ks]) =
+                make_float4(e[nt][0], e[nt][1], e[nt][2], e[nt][3]);
+            tmax[j][4 * wave + ks][h] = mx;
           }
         }
       }
     }
+  };
+  for (int j0 = 0; j0 < nbl; j0 += 8) {
+    if (j0 + 4 < nbl) load_batch(j0 + 4, cwB, zwB);
+    scan_batch(j0, cwA, zwA);
+    if (j0 + 4 >= nbl) break;
+    if (j0 + 8 < nbl) load_batch(j0 + 8, cwA, zwA);
+    scan_batch(j0 + 4, cwB, zwB);
   }
   __syncthreads();
 
@@ -438,7 +509,10 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
       kp = blk < sink_end || blk >= local_beg;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float bm = fmaxf(fmaxf(tmax[lane][0][h], tmax[lane][1][h]), fmaxf(tmax[lane][2][h], tmax[lane][3][h]));
+        float bm = tmax[lane][0][h];
+#pragma unroll
+        for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tmax[lane][r][h]);
+        bm *= scale4;
         kp = kp || (bm >= thr_s[h]);
         if (p.dbg_bmax) p.dbg_bmax[((size_t)b * p.Hq + qh0 + h) * p.nblk_cap + blk] = bm;
       }
@@ -457,17 +531,11 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   float* pwv = pw[wave];
   {
     const int co = lane & 15, tp = lane >> 4;
-    const int t_a = 16 * wave + col;  // token of this lane's A-fragment row
-    uint2 R[kGroups];
-    uint2 S8;
+    uint2 R[kGroups], S8;
     uint4 Vr[4];
     auto load_block = [&](int j) {
-      const size_t bi = head * p.nblk_cap + blk0 + j;
-      const int8_t* rb = p.res + bi * kResBytes;
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g)
-        R[g] = *reinterpret_cast<const uint2*>(rb + ((2 * g + (ks >> 1)) * 64 + t_a) * 16 + 8 * (ks & 1));
-      S8 = *reinterpret_cast<const uint2*>(p.rsc + bi * kRscBytes + (gc * 64 + 16 * wave + 4 * ks) * 2);
+      const size_t bi = bi0 + j;
+      load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, R, S8);
       const uint16_t* vb = p.v + ((head * p.L_cap + (size_t)(blk0 + j) * 64 + 16 * wave + tp) * kHeadDim + 8 * co);
 #pragma unroll
       for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
@@ -475,9 +543,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
     if (K > 0) load_block(klist[0]);
     for (int kk = 0; kk < K; ++kk) {
       const int j = klist[kk];
-      const int row_base = (blk0 + j) * 64 + 16 * wave;
-      const int n_rows = min(16, L - row_base);
-      // current block's registers; the next kept block is loaded meanwhile
+      const int n_rows = min(16, L - ((blk0 + j) * 64 + 16 * wave));
       uint2 Rc[kGroups];
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) Rc[g] = R[g];
@@ -488,26 +554,18 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
       if (kk + 1 < K) load_block(klist[kk + 1]);
       if (n_rows <= 0) continue;  // this wave's tile lies past the sequence end
 
-      const h8 r0 = unpack_res(Rc[0]), r1 = unpack_res(Rc[1]), r2 = unpack_res(Rc[2]), r3 = unpack_res(Rc[3]);
-      const float s8r[4] = {lo_h(S8c.x), hi_h(S8c.x), lo_h(S8c.y), hi_h(S8c.y)};
+      float r[NT][4];
+      qf.residual(Rc, S8c, p.sm_scale, r);
       float alpha_l[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        f4 c = {c_res[nt], c_res[nt], c_res[nt], c_res[nt]};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(r0, Bf[nt][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(r1, Bf[nt][1], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(r2, Bf[nt][2], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(r3, Bf[nt][3], c, 0, 0, 0);
         const int h = 4 * nt + hc;
         const int hh = h < G ? h : 0;
         const float4 e4 = *reinterpret_cast<const float4*>(&u.est[j][wave][hh][4 * ks]);
         const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
         float s[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float rterm = quad_sum(s8r[i] * c[i]);
-          s[i] = (4 * ks + i < n_rows) ? fmaf(p.sm_scale, rterm, ev[i]) : -INFINITY;
-        }
+        for (int i = 0; i < 4; ++i) s[i] = (4 * ks + i < n_rows) ? fmaf(ev[i], scale4, r[nt][i]) : -INFINITY;
         alpha_l[nt] = st.fold(nt, s, pwv, PG, hh, gc == 0 && h < G, ks);
       }
       float alpha[G];
@@ -525,7 +583,7 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   for (int nt = 0; nt < NT; ++nt) {
     hm[nt] = st.m[nt];
     hl[nt] = st.l[nt];
-    hidx[nt] = 4 * nt + hc;
+    hidx[nt] = 4 * nt + hc < G ? 4 * nt + hc : 0;
     hw[nt] = (lane < 16) && (gc == 0) && (4 * nt + hc < G);
   }
   finish_chunk<G, NT>(p, u.cl, st.acc, wave, lane, tid, b, hkv, chunk, hm, hl, hidx, hw);
@@ -533,29 +591,41 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------
 // Dense flash-decode over fp16 K/V (speed baseline) with the same chunking,
-// softmax, P.V, combine and merge kernel.  QK on MFMA: A = K tile (16 tokens x 32
-// channels per group), B = q with one column per head.
+// softmax, P.V, combine and merge kernel.  QK on MFMA: A = K tile (16 tokens x
+// 32 channels per group), B = q with one column per head.
 // ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
   constexpr int PG = (G + 3) & ~3;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int L = clamp_len(p, b);
-  const int nblk = (L + 63) >> 6;
   const int blk0 = chunk * p.cb;
-  if (blk0 >= nblk) return;
-  const int nbl = min(p.cb, nblk - blk0);
+  const int nbl_cap = min(p.cb, p.nblk_cap - blk0);
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
+  const int col = lane & 15, ks = lane >> 4;
+  const int co = lane & 15, tp = lane >> 4;
+  const int t_a = 16 * wave + col;
+  uint4 Kr[kGroups], Vr[4];
+  auto load_block = [&](int j) {
+    const size_t row = head * p.L_cap + (size_t)(blk0 + min(j, nbl_cap - 1)) * 64;
+    const uint16_t* kb = p.k + (row + t_a) * kHeadDim + 8 * ks;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) Kr[g] = *reinterpret_cast<const uint4*>(kb + 32 * g);
+    const uint16_t* vb = p.v + (row + 16 * wave + tp) * kHeadDim + 8 * co;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
+  };
+  load_block(0);
   __shared__ h2 q2[G][64];
   __shared__ float pw[kWaves][16 * PG];
   __shared__ CombineLds<G> cl;
-  for (int i = tid; i < G * 64; i += 256)
-    q2[i >> 6][i & 63] = __builtin_bit_cast(
-        h2, *reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + qh0 + (i >> 6)) * kHeadDim + 2 * (i & 63)));
+  stage_q<G>(p, b, qh0, tid, q2);
+  const int L = clamp_len(p, b);
+  const int nblk = (L + 63) >> 6;
+  if (blk0 >= nblk) return;
+  const int nbl = min(p.cb, nblk - blk0);
   __syncthreads();
-  const int col = lane & 15, ks = lane >> 4;
   h8 Bd[kGroups];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
@@ -572,22 +642,8 @@ __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
   WaveSoftmax<G, 1> st;
   st.init();
   float* pwv = pw[wave];
-  const int co = lane & 15, tp = lane >> 4;
-  const int t_a = 16 * wave + col;
-  uint4 Kr[kGroups], Vr[4];
-  auto load_block = [&](int j) {
-    const size_t row = head * p.L_cap + (size_t)(blk0 + j) * 64;
-    const uint16_t* kb = p.k + (row + t_a) * kHeadDim + 8 * ks;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) Kr[g] = *reinterpret_cast<const uint4*>(kb + 32 * g);
-    const uint16_t* vb = p.v + (row + 16 * wave + tp) * kHeadDim + 8 * co;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
-  };
-  load_block(0);
   for (int j = 0; j < nbl; ++j) {
-    const int row_base = (blk0 + j) * 64 + 16 * wave;
-    const int n_rows = min(16, L - row_base);
+    const int n_rows = min(16, L - ((blk0 + j) * 64 + 16 * wave));
     uint4 Kc[kGroups], Vc[4];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) Kc[g] = Kr[g];
@@ -618,63 +674,66 @@ __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Log-sum-exp merge of the chunk partials -> fp16 out:
 //   M = max_c m_c,  out = sum_c o_c e^{m_c - M} / sum_c l_c e^{m_c - M}.
-// Grid (Hq, B, 4): work-group = one query head, 32 output channels; its 256
-// threads are 8 chunk phases x 32 channels, chunk weights staged in LDS.
+// Grid (Hq, B, 4): work-group = one query head, 32 output channels; thread =
+// (chunk phase cp = tid/32, channel).  Partials are read in pieces of 256
+// chunks, all loads of a piece issued together, with an online rescale across
+// pieces.  Chunks that kept nothing have weight 0 (selected, never
+// multiplied, so their unwritten o is never used).
 // ---------------------------------------------------------------------------
-constexpr int kMergePiece = 1024;
-
 __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
-  __shared__ float wts[kMergePiece];
-  __shared__ float red[8][33];
-  __shared__ float Msh, Lsh;
+  constexpr int kPiece = 256;
+  constexpr int kPer = kPiece / 8;
+  __shared__ float wts[kPiece];
+  __shared__ float red[8][32];
+  __shared__ float wmax[kWaves];
+  __shared__ float wsum[kWaves];
   const int h = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = clamp_len(p, b);
-  const int nblk = (L + 63) >> 6;
-  const int nch = (nblk + p.cb - 1) / p.cb;
+  const int cp = tid >> 5, ch = 32 * slice + (tid & 31);
   const size_t row = (size_t)b * p.Hq + h;
   const float2* ml = p.part_ml + row * p.nchunk;
-  float m = -INFINITY;
-  for (int c = tid; c < nch; c += 256) {
-    const float2 v = ml[c];
-    if (v.y > 0.f) m = fmaxf(m, v.x);
-  }
-  m = wave_max(m);
-  if (lane == 0) red[0][wave] = m;
-  __syncthreads();
-  if (tid == 0) Msh = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-  __syncthreads();
-  const float M = Msh;
-  const int cp = tid >> 5, ch = 32 * slice + (tid & 31);
   const float* po = p.part_o + row * p.nchunk * kHeadDim + ch;
-  float o = 0.f, ls = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += kMergePiece) {
-    const int n = min(kMergePiece, nch - c0);
+  const int L = clamp_len(p, b);
+  const int nch = (((L + 63) >> 6) + p.cb - 1) / p.cb;
+  float M = -INFINITY, o = 0.f, ls = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += kPiece) {
+    const int n = min(kPiece, nch - c0);
+    const float2 v = tid < n ? ml[c0 + tid] : make_float2(-INFINITY, 0.f);
+    float x[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = cp + 8 * i;
+      x[i] = c < n ? po[(size_t)(c0 + c) * kHeadDim] : 0.f;
+    }
+    const bool live = v.y > 0.f;
+    float mp = wave_max(live ? v.x : -INFINITY);
+    if (lane == 0) wmax[wave] = mp;
     __syncthreads();
-    for (int c = tid; c < n; c += 256) {
-      const float2 v = ml[c0 + c];
-      const float w = v.y > 0.f ? exp2f((v.x - M) * kLog2e) : 0.f;
-      wts[c] = w;
-      ls += w * (v.y > 0.f ? v.y : 0.f);
+    mp = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float Mn = fmaxf(M, mp);
+    const float w = live ? exp2f((v.x - Mn) * kLog2e) : 0.f;
+    wts[tid] = w;
+    const float sc = M > -INFINITY ? exp2f((M - Mn) * kLog2e) : 0.f;
+    ls = ls * sc + (live ? w * v.y : 0.f);
+    o *= sc;
+    M = Mn;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const float wi = wts[cp + 8 * i];
+      o = wi > 0.f ? fmaf(wi, x[i], o) : o;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int c = cp; c < n; c += 8) {
-      const float w = wts[c];
-      if (w > 0.f) o = fmaf(w, po[(size_t)(c0 + c) * kHeadDim], o);
-    }
   }
   ls = wave_sum(ls);
-  __syncthreads();
   red[cp][tid & 31] = o;
-  __syncthreads();
-  if (lane == 0) wts[wave] = ls;
+  if (lane == 0) wsum[wave] = ls;
   __syncthreads();
   if (tid < 32) {
     float acc = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc += red[q][tid];
-    const float lsum = (wts[0] + wts[1]) + (wts[2] + wts[3]);
+    const float lsum = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     p.out[row * kHeadDim + ch] = __builtin_bit_cast(uint16_t, (_Float16)(acc / lsum));
   }
 }

@@ -59,6 +59,42 @@ constexpr int kRowMirror = 0x140;
 
 __device__ inline float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48)
+// with the gfx950 row-swap permutes; every lane receives the result.  The swap
+// is written as inline asm (with the wait states it needs around it): the
+// compiler's builtin form folds the two swapped halves of a float into one.
+__device__ inline void swap_rows32(uint32_t& x, uint32_t& y) {  // x.hi32 <-> y.lo32
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ inline void swap_rows16(uint32_t& x, uint32_t& y) {  // x.odd rows <-> y.even rows
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ inline float rows_max(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap_rows32(x, y);
+  v = fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+  x = __builtin_bit_cast(uint32_t, v);
+  y = x;
+  swap_rows16(x, y);
+  return fmaxf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y));
+}
+__device__ inline float rows_sum(float v) {
+  uint32_t x = __builtin_bit_cast(uint32_t, v), y = x;
+  swap_rows32(x, y);
+  v = __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+  x = __builtin_bit_cast(uint32_t, v);
+  y = x;
+  swap_rows16(x, y);
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
+// (x & mask) | bits in one VALU op (the compiler splits it into two)
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "s"(mask), "v"(bits));
+  return d;
+}
+
 // maximum over all 64 lanes, returned in every lane
 __device__ inline float wave_max(float v) {
   v = fmaxf(v, dpp<kQuadXor1>(v));
