@@ -43,7 +43,42 @@ REFINE_BYTES = 392   # int8 residual 128 B + rscale 8 B + fp16 V 256 B per kept 
 PSEUDO_BYTES = 184   # packed K (codes, scale/zero, residual, rscale) per support token-head
 DENSE_BYTES = 512    # fp16 K + V per token-head
 ROTATE_TARGET = 1.5e9
+# HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
+# `bench.py --workload W --no-long --no-cpu-baseline --steps 20 --warmup 5`
+# (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, mean over the attend
+# dispatches).  Both counters are scaled by what they read for the plain
+# 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088 KiB
+# for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
+# while the kernel sources hash to the digest it was recorded with.
+FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
+TRAFFIC_KIB = {
+    "llama8b_16k": {"sources": "bf3d00b3c1ed8a13", "fetch": 9922.32, "write": 666.18},
+    "long_256k": {"sources": "bf3d00b3c1ed8a13", "fetch": 133507.83, "write": 3314.65},
+}
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
+
+
+def kernel_digest() -> str:
+    """sha256 over the HIP sources, the public header and the build script."""
+    import hashlib
+    pkg = os.path.join(ROOT, "sparse_long_context_ffd_amd")
+    files = sorted(os.path.join(pkg, "csrc", f) for f in os.listdir(os.path.join(pkg, "csrc")))
+    files += [os.path.join(pkg, "build.py"), os.path.join(ROOT, "include", "ffd.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload: str):
+    """Profiled HBM bytes per fused-kernel launch, or None when none were
+    recorded for this workload with the current kernel sources."""
+    t = TRAFFIC_KIB.get(workload)
+    if t is None or t["sources"] != kernel_digest():
+        return None
+    return int(round((t["fetch"] * FETCH_SCALE + t["write"] * WRITE_SCALE) * 1024))
 
 
 def graph_of(calls, torch):
@@ -222,6 +257,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-long", action="store_true", help="skip the 256K FFD vs dense leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=256,
+                    help="size of one plain device-to-device copy done before timing; profiles scale "
+                         "the HBM byte counters by what they read for it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
@@ -240,6 +278,13 @@ def main():
     w = WORKLOADS[args.workload]
     delta = w.deltas[0] if args.delta is None else args.delta
 
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     c, d = prepare(w, args.seed, torch)
     r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale)
     dense = measure_dense(w, args.steps, args.warmup, d, torch, sm_scale)
@@ -267,9 +312,9 @@ def main():
         "dense_us_per_step": round(dense["us_per_step"], 3),
         "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes(w.name),
                      "kernel": "attend_kernel (fused Top-delta scan + refine)",
-                     "bytes_per_launch": r["attend_bytes"]},
+                     "bytes_per_launch": r["attend_bytes"], "kernel_sources": kernel_digest()},
     }
     del d
     torch.cuda.empty_cache()
@@ -284,7 +329,8 @@ def main():
             "workload": wl.name, "delta": wl.deltas[0], "us_per_step": round(rl["us_per_step"], 3),
             "keep_fraction": round(rl["keep_fraction"], 5), "attend_kernel_us": round(rl["attend_us_mean"], 3),
             "effective_gbps": round(rl["step_bytes"] / (rl["us_per_step"] * 1e3), 1),
-            "roofline_attend": {"achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4)},
+            "roofline_attend": {"achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
+                                "traffic": traffic_bytes(wl.name), "bytes_per_launch": rl["attend_bytes"]},
             "dense_us_per_step": round(dn["us_per_step"], 3), "dense_gbps": round(dn["gbps"], 1),
             "speedup_vs_dense": round(dn["us_per_step"] / rl["us_per_step"], 3),
             "layers_rotated": rl["layers_rotated"], "chunk_blocks": rl["plan"][0],
