@@ -121,8 +121,9 @@ def prepare(w, seed, torch):
 def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     import sparse_long_context_ffd_amd as ffd
     shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
-    base = ffd.PackedCache(shape, v=d["v"])
+    base = ffd.PackedCache(shape)
     ffd.quantize_k(shape, d["k"], 0, w.max_len, base)
+    ffd.pack_v(shape, d["v"], 0, w.max_len, base)
     ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
     nb = w.max_len // 64
@@ -143,16 +144,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     support = sum(min(int(L), w.sink + w.local) for L in lens) * w.kv_heads
     step_bytes = attend_bytes + PSEUDO_BYTES * support
 
-    layer_bytes = sum(getattr(base, f).numel() for f in ("codes", "sz", "res", "rscale")) + d["v"].numel() * 2
+    layer_bytes = sum(n for n in ffd.cache_bytes(shape).values())
     R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
-    layers = [base]
-    for _ in range(R - 1):
-        cc = ffd.PackedCache.__new__(ffd.PackedCache)
-        cc.shape = shape
-        for f in ("codes", "sz", "res", "rscale"):
-            setattr(cc, f, getattr(base, f).clone())
-        cc.v = d["v"].clone()
-        layers.append(cc)
+    layers = [base] + [base.clone() for _ in range(R - 1)]
     log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
 
     def step(i, stages=0):

@@ -93,7 +93,10 @@ typedef struct ffd_shape {
  *              ((ch/16)*64 + t)*16 + ch%16   (two's complement).
  *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t, group g at
  *              element g*64 + t.
- *  v       fp16   [B][Hkv][max_seq_len][128] values, natural row-major layout.
+ *  v       fp16   [B][Hkv][max_seq_len*128]  values, token-quad tiled: token
+ *          t, channel ch at element ((t/4)*128 + ch)*4 + t%4 (so the four
+ *          tokens 4j..4j+3 of one channel are 8 contiguous bytes; one 64-token
+ *          block is 16384 contiguous bytes).  Written by ffd_pack_v.
  *
  * Positions the pack never wrote (beyond the sequence) may hold any bytes:
  * decode masks them before any arithmetic that could propagate them. */
@@ -102,7 +105,7 @@ typedef struct ffd_cache {
   void* sz;
   void* res;
   void* rscale;
-  const void* v;
+  void* v;
 } ffd_cache_t;
 
 /* Optional diagnostics of ffd_decode_attn (each pointer may be NULL).
@@ -126,7 +129,7 @@ typedef struct ffd_debug {
 
 /* Bytes of each packed-cache field for `shape` (host call, no GPU work). */
 int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes,
-                    size_t* res_bytes, size_t* rscale_bytes);
+                    size_t* res_bytes, size_t* rscale_bytes, size_t* v_bytes);
 
 /* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
  * (host call).  The workspace holds partial pseudo-maxima and per-chunk
@@ -146,6 +149,15 @@ int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks)
  * Byte-exact with the conventions above. */
 int ffd_quantize_k(const ffd_shape_t* shape, const void* k, int32_t t_begin, int32_t t_end,
                    const ffd_cache_t* cache, void* stream);
+
+/* Value store for the refinement (Method 3, stage 3 loads the values of the
+ * selected blocks): copy tokens [t_begin, t_end) of every (b, kv head) of `v`
+ * (fp16 [B][Hkv][max_seq_len][128], natural row-major, 16-byte aligned) into
+ * cache->v in the tiled layout above.  The fp16 values are unchanged; only
+ * their order differs.  Same range rules as ffd_quantize_k (other positions
+ * untouched; t_end = t_begin + 1 appends one token); only cache->v is used. */
+int ffd_pack_v(const ffd_shape_t* shape, const void* v, int32_t t_begin, int32_t t_end,
+               const ffd_cache_t* cache, void* stream);
 
 /* One FFD decode-attention step (Method 3 stages 1-3 plus the log-sum-exp
  * merge of per-chunk partials).

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     dense_decode_attn,
     lib,
     make_shape,
+    pack_v,
     plan,
     quantize_k,
     strerror,
@@ -22,5 +23,5 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "cache_bytes", "decode_attn",
-    "dense_decode_attn", "lib", "make_shape", "plan", "quantize_k", "strerror", "workspace_bytes",
+    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "quantize_k", "strerror", "workspace_bytes",
 ]

@@ -20,7 +20,7 @@ STATUS = {
     -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP",
 }
 EXPORTED = (
-    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_decode_attn",
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_decode_attn",
     "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
 )
 
@@ -58,10 +58,11 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m sparse_long_context_ffd_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, V, SZ, I32 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
-        L.ffd_cache_bytes.argtypes = [P(Shape), P(SZ), P(SZ), P(SZ), P(SZ)]
+        L.ffd_cache_bytes.argtypes = [P(Shape), P(SZ), P(SZ), P(SZ), P(SZ), P(SZ)]
         L.ffd_workspace_bytes.argtypes = [P(Shape), P(SZ)]
         L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
+        L.ffd_pack_v.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_decode_attn.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, V, V, SZ,
                                       P(Debug), V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
@@ -89,11 +90,13 @@ def make_shape(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int
     return Shape(batch, num_q_heads, num_kv_heads, head_dim, block, sink, local, max_seq_len, chunk_blocks)
 
 
+FIELDS = ("codes", "sz", "res", "rscale", "v")
+
+
 def cache_bytes(shape: Shape) -> dict:
-    a, b, c, d = (ctypes.c_size_t() for _ in range(4))
-    _check(lib().ffd_cache_bytes(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
-                                 ctypes.byref(d)), "ffd_cache_bytes")
-    return {"codes": a.value, "sz": b.value, "res": c.value, "rscale": d.value}
+    n = [ctypes.c_size_t() for _ in FIELDS]
+    _check(lib().ffd_cache_bytes(ctypes.byref(shape), *(ctypes.byref(x) for x in n)), "ffd_cache_bytes")
+    return {f: x.value for f, x in zip(FIELDS, n)}
 
 
 def workspace_bytes(shape: Shape) -> int:
@@ -128,22 +131,27 @@ def _need(t, dtype, numel, name):
 
 
 class PackedCache:
-    """Device buffers of one layer's packed FFD cache (plus the caller's fp16 V)."""
+    """Device buffers (uint8 tensors) of one layer's FFD cache: the packed K
+    fields and the tiled fp16 V, layouts as in include/ffd.h."""
 
-    def __init__(self, shape: Shape, v=None, device="cuda"):
+    def __init__(self, shape: Shape, device="cuda"):
         import torch
         nb = cache_bytes(shape)
         self.shape = shape
-        self.codes = torch.empty(nb["codes"], dtype=torch.uint8, device=device)
-        self.sz = torch.empty(nb["sz"], dtype=torch.uint8, device=device)
-        self.res = torch.empty(nb["res"], dtype=torch.uint8, device=device)
-        self.rscale = torch.empty(nb["rscale"], dtype=torch.uint8, device=device)
-        self.v = v
+        for f in FIELDS:
+            setattr(self, f, torch.empty(nb[f], dtype=torch.uint8, device=device))
 
     def fill_(self, byte: int) -> "PackedCache":
-        for t in (self.codes, self.sz, self.res, self.rscale):
-            t.fill_(byte)
+        for f in FIELDS:
+            getattr(self, f).fill_(byte)
         return self
+
+    def clone(self) -> "PackedCache":
+        c = PackedCache.__new__(PackedCache)
+        c.shape = self.shape
+        for f in FIELDS:
+            setattr(c, f, getattr(self, f).clone())
+        return c
 
     def c_struct(self) -> Cache:
         return Cache(_ptr(self.codes), _ptr(self.sz), _ptr(self.res), _ptr(self.rscale), _ptr(self.v))
@@ -157,6 +165,14 @@ def quantize_k(shape: Shape, k, t_begin: int, t_end: int, cache: PackedCache, st
                                 _stream(stream)), "ffd_quantize_k")
 
 
+def pack_v(shape: Shape, v, t_begin: int, t_end: int, cache: PackedCache, stream=None) -> None:
+    import torch
+    _need(v, torch.float16, shape.batch * shape.num_kv_heads * shape.max_seq_len * 128, "v")
+    c = cache.c_struct()
+    _check(lib().ffd_pack_v(ctypes.byref(shape), _ptr(v), int(t_begin), int(t_end), ctypes.byref(c),
+                            _stream(stream)), "ffd_pack_v")
+
+
 def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,
                 workspace, debug: Optional[dict] = None, stream=None) -> None:
     import torch
@@ -164,7 +180,9 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
     _need(q, torch.float16, rows * 128, "q")
     _need(out, torch.float16, rows * 128, "out")
     _need(seq_lens, torch.int32, shape.batch, "seq_lens")
-    _need(cache.v, torch.float16, shape.batch * shape.num_kv_heads * shape.max_seq_len * 128, "cache.v")
+    nb = cache_bytes(shape)
+    for f in FIELDS:
+        _need(getattr(cache, f), torch.uint8, nb[f], f"cache.{f}")
     _need(workspace, torch.uint8, 0, "workspace")
     c = cache.c_struct()
     dbg = None

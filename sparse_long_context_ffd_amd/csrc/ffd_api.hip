@@ -84,7 +84,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 extern "C" {
 
-int ffd_version(void) { return 100; }
+int ffd_version(void) { return 200; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -101,15 +101,16 @@ const char* ffd_strerror(int code) {
 }
 
 int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes, size_t* res_bytes,
-                    size_t* rscale_bytes) {
+                    size_t* rscale_bytes, size_t* v_bytes) {
   const int st = check_shape(shape);
   if (st) return st;
-  if (!codes_bytes || !sz_bytes || !res_bytes || !rscale_bytes) return FFD_ERR_NULL;
+  if (!codes_bytes || !sz_bytes || !res_bytes || !rscale_bytes || !v_bytes) return FFD_ERR_NULL;
   const size_t blocks = (size_t)shape->batch * shape->num_kv_heads * (shape->max_seq_len / 64);
   *codes_bytes = blocks * ffd::kCodesBytes;
   *sz_bytes = blocks * ffd::kSzBytes;
   *res_bytes = blocks * ffd::kResBytes;
   *rscale_bytes = blocks * ffd::kRscBytes;
+  *v_bytes = blocks * ffd::kVBytes;
   return FFD_OK;
 }
 
@@ -144,6 +145,18 @@ int ffd_quantize_k(const ffd_shape_t* shape, const void* k, int32_t t_begin, int
   return from_hip(ffd::launch_pack(k, shape->batch, shape->num_kv_heads, shape->max_seq_len, t_begin, t_end,
                                    cache->codes, cache->sz, cache->res, cache->rscale,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int ffd_pack_v(const ffd_shape_t* shape, const void* v, int32_t t_begin, int32_t t_end, const ffd_cache_t* cache,
+               void* stream) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!v || !cache || !cache->v) return FFD_ERR_NULL;
+  if (!aligned16(v) || !aligned16(cache->v)) return FFD_ERR_ALIGN;
+  if (t_begin < 0 || t_end < t_begin || t_end > shape->max_seq_len) return FFD_ERR_ARG;
+  if (t_end == t_begin) return FFD_OK;
+  return from_hip(ffd::launch_pack_v(v, shape->batch, shape->num_kv_heads, shape->max_seq_len, t_begin, t_end,
+                                     cache->v, static_cast<hipStream_t>(stream)));
 }
 
 int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,

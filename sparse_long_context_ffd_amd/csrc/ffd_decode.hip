@@ -335,34 +335,10 @@ struct CombineLds {
   float o[kWaves][G][kHeadDim];
 };
 
-// Combine the 4 waves' states into the chunk partial (o[128], m, l) per query
-// head.  `head_m`/`head_l` are the lane's state for head `lane_head[n]`,
-// stored when `state_writer[n]`.
-template <int G, int NS>
-__device__ void finish_chunk(const DecodeParams& p, CombineLds<G>& cl, float (&acc)[G][8], int wave, int lane,
-                             int tid, int b, int hkv, int chunk, const float (&head_m)[NS],
-                             const float (&head_l)[NS], const int (&lane_head)[NS], const bool (&state_writer)[NS]) {
-  // reduce acc over the 4 row phases; lanes 0..15 then hold 8 channels each
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      acc[h][k] = rows_sum(acc[h][k]);
-    }
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(&cl.o[wave][h][8 * lane]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(&cl.o[wave][h][8 * lane + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < NS; ++n)
-    if (state_writer[n]) {
-      cl.m[wave][lane_head[n]] = head_m[n];
-      cl.l[wave][lane_head[n]] = head_l[n];
-    }
-  __syncthreads();
+// Combine the 4 waves' states (stored in `cl`) into the chunk partial
+// (o[128], m, l) of every query head of the group.
+template <int G>
+__device__ void combine_chunk(const DecodeParams& p, const CombineLds<G>& cl, int tid, int b, int hkv, int chunk) {
   const int qh0 = hkv * G;
   for (int i = tid; i < G * kHeadDim; i += 256) {
     const int h = i >> 7, ch = i & 127;
@@ -385,25 +361,161 @@ __device__ void finish_chunk(const DecodeParams& p, CombineLds<G>& cl, float (&a
   }
 }
 
+// Dense kernel's end of chunk: reduce acc over the 4 row phases (lanes 0..15
+// then hold 8 channels each), store the wave states, combine.  `head_m`/`head_l`
+// are the lane's state for head `lane_head[n]`, stored when `state_writer[n]`.
+template <int G, int NS>
+__device__ void finish_chunk(const DecodeParams& p, CombineLds<G>& cl, float (&acc)[G][8], int wave, int lane,
+                             int tid, int b, int hkv, int chunk, const float (&head_m)[NS],
+                             const float (&head_l)[NS], const int (&lane_head)[NS], const bool (&state_writer)[NS]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      acc[h][k] = rows_sum(acc[h][k]);
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *reinterpret_cast<float4*>(&cl.o[wave][h][8 * lane]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(&cl.o[wave][h][8 * lane + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NS; ++n)
+    if (state_writer[n]) {
+      cl.m[wave][lane_head[n]] = head_m[n];
+      cl.l[wave][lane_head[n]] = head_l[n];
+    }
+  __syncthreads();
+  combine_chunk<G>(p, cl, tid, b, hkv, chunk);
+}
+
+// ---------------------------------------------------------------------------
+// Refinement state of one wave, P.V on MFMA 16x16x16 f16 as O^T = V^T P^T:
+//   A = V^T: lane (m = lane&15, ks = lane>>4) holds channel 8m + jm of tile
+//       tokens 4ks..4ks+3 for MFMA jm = 0..7 (8 contiguous bytes of the
+//       token-quad tiled V);
+//   B = P^T: tile tokens 4ks..4ks+3 of column col = lane&15, i.e. exactly the
+//       lane's own softmax weights in the score MFMA's C layout;
+//   C: lane holds O[channel 32ks + 8i + jm][col] for i = 0..3.
+// The four group columns 4h..4h+3 of a head carry identical copies.  P is
+// split into fp16 hi + lo parts (two MFMAs each), so the product keeps about
+// 21 bits of the fp32 weights.
+// ---------------------------------------------------------------------------
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+template <int NT>
+struct MfmaSoftmax {
+  float m[NT], l[NT];  // running max and sum of the lane column's head
+  f4 o[NT][8];
+  __device__ void init() {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      m[n] = -INFINITY;
+      l[n] = 0.f;
+#pragma unroll
+      for (int jm = 0; jm < 8; ++jm) o[n][jm] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  // fold one tile: s = scores of the lane's 4 rows per column tile (rows past
+  // the sequence end -inf), va = V^T fragments (rows past the end zeroed)
+  __device__ void step(const float (&s)[NT][4], const h4 (&va)[8]) {
+    float alpha[NT];
+    h4 bhi[NT], blo[NT];
+    bool moved = false;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float tm = rows_max(fmaxf(fmaxf(s[n][0], s[n][1]), fmaxf(s[n][2], s[n][3])));
+      const float mn = fmaxf(m[n], tm);
+      const float mr = mn == -INFINITY ? 0.f : mn;
+      alpha[n] = __builtin_amdgcn_exp2f((m[n] - mr) * kLog2e);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f((s[n][i] - mr) * kLog2e);
+      l[n] = fmaf(l[n], alpha[n], rows_sum((pr[0] + pr[1]) + (pr[2] + pr[3])));
+      m[n] = mn;
+      moved = moved || (alpha[n] != 1.f);
+      const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]));
+      const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]));
+      const h2 l01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01.x, pr[1] - (float)h01.y));
+      const h2 l23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23.x, pr[3] - (float)h23.y));
+      bhi[n] = h4{h01.x, h01.y, h23.x, h23.y};
+      blo[n] = h4{l01.x, l01.y, l23.x, l23.y};
+    }
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rescale only when some head's max moved
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int jm = 0; jm < 8; ++jm) o[n][jm] *= alpha[n];
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int jm = 0; jm < 8; ++jm) {
+        o[n][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], bhi[n], o[n][jm], 0, 0, 0);
+        o[n][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], blo[n], o[n][jm], 0, 0, 0);
+      }
+  }
+  // store the wave's state for the combine: lanes of group column 0 of each
+  // live head write its 128 channels (32 per row group ks) and m, l
+  template <int G>
+  __device__ void store(CombineLds<G>& cl, int wave, int lane) const {
+    const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int h = 4 * n + hc;
+      if (gc == 0 && h < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float* dst = &cl.o[wave][h][32 * ks + 8 * i];
+          *reinterpret_cast<float4*>(dst) = make_float4(o[n][0][i], o[n][1][i], o[n][2][i], o[n][3][i]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[n][4][i], o[n][5][i], o[n][6][i], o[n][7][i]);
+        }
+        if (ks == 0) {
+          cl.m[wave][h] = m[n];
+          cl.l[wave][h] = l[n];
+        }
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Stages 2 + 3 for one chunk of blocks.
 //   phase A: every wave estimates its tile of every block of the chunk (loads
 //            double-buffered in batches of 4 blocks); estimates stay in LDS
 //   decide:  block kept if it holds a support token, or some head's block
 //            max of the estimate reaches that head's threshold
-//   phase B: every wave refines its tile of every kept block (next kept
-//            block prefetched), online softmax, P.V
+//   phase B: every wave refines its tile of every kept block (residual, rscale
+//            and V of the next kept block loaded while the current one is
+//            computed), online softmax, P.V on MFMA
+// Dynamic LDS: per-block estimates [cb][4 waves][G][16] (reused by the
+// combine) followed by per-(block, wave, row group) maxima [cb][16][G].
 // ---------------------------------------------------------------------------
 template <int G>
 struct AttendCfg {
   static constexpr int NT = QFrags<G>::NT;
-  static constexpr int PG = (G + 3) & ~3;
   static constexpr int CBMAX = (G <= 4) ? 32 : 16;
+  static constexpr size_t est_bytes(int cb) { return (size_t)cb * kWaves * G * 16 * sizeof(float); }
+  static constexpr size_t lds_bytes(int cb) {
+    return (est_bytes(cb) > sizeof(CombineLds<G>) ? est_bytes(cb) : sizeof(CombineLds<G>)) +
+           (size_t)cb * 4 * kWaves * G * sizeof(float);
+  }
 };
 
+struct RefineRegs {
+  uint2 R[kGroups];
+  uint2 S8;
+  uint4 V[4];
+};
+
+// Register budget: 3 waves per SIMD for G <= 4 (<= 168 VGPRs, no spills); the
+// G > 4 variant keeps twice the accumulators and runs at 2.
 template <int G>
-__global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
-  constexpr int NT = AttendCfg<G>::NT, PG = AttendCfg<G>::PG, CBMAX = AttendCfg<G>::CBMAX;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void attend_kernel(
+    DecodeParams p) {
+  constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int blk0 = chunk * p.cb;
@@ -431,14 +543,14 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   __shared__ h2 q2[G][64];
   __shared__ float qg[G][kGroups];
   __shared__ float thr_s[G];
-  __shared__ float tmax[CBMAX][4 * kWaves][G];  // per (block, wave, row group) maxima
   __shared__ int klist[CBMAX];
   __shared__ int nkeep;
-  __shared__ float pw[kWaves][16 * PG];
-  __shared__ union U {
-    float est[CBMAX][kWaves][G][16];
-    CombineLds<G> cl;
-  } u;
+  extern __shared__ __align__(16) float dyn[];
+  const int cb = p.cb;
+  float* est = dyn;                                                // [cb][kWaves][G][16]
+  float* tmax = dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float);  // [cb][4*kWaves][G]
+  if (AttendCfg<G>::est_bytes(cb) < sizeof(CombineLds<G>)) tmax = dyn + sizeof(CombineLds<G>) / sizeof(float);
+  CombineLds<G>& cl = *reinterpret_cast<CombineLds<G>*>(dyn);
 
   stage_q<G>(p, b, qh0, tid, q2);
   float mt = -INFINITY;  // pseudo-max of head `tid`: max over the parts (loads issued with the others)
@@ -482,9 +594,9 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
           const float mx = fmaxf(fmaxf(e[nt][0], e[nt][1]), fmaxf(e[nt][2], e[nt][3]));
           const int h = 4 * nt + hc;
           if (gc == 0 && h < G) {
-            *reinterpret_cast<float4*>(&u.est[j][wave][h][4 * ks]) =
+            *reinterpret_cast<float4*>(&est[((j * kWaves + wave) * G + h) * 16 + 4 * ks]) =
                 make_float4(e[nt][0], e[nt][1], e[nt][2], e[nt][3]);
-            tmax[j][4 * wave + ks][h] = mx;
+            tmax[(j * 4 * kWaves + 4 * wave + ks) * G + h] = mx;
           }
         }
       }
@@ -509,9 +621,10 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
       kp = blk < sink_end || blk >= local_beg;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float bm = tmax[lane][0][h];
+        const float* tm = tmax + lane * 4 * kWaves * G + h;
+        float bm = tm[0];
 #pragma unroll
-        for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tmax[lane][r][h]);
+        for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tm[r * G]);
         bm *= scale4;
         kp = kp || (bm >= thr_s[h]);
         if (p.dbg_bmax) p.dbg_bmax[((size_t)b * p.Hq + qh0 + h) * p.nblk_cap + blk] = bm;
@@ -526,67 +639,69 @@ __global__ __launch_bounds__(256) void attend_kernel(DecodeParams p) {
   const int K = nkeep;
 
   // ---- phase B: refine tile `wave` of every kept block ----
-  WaveSoftmax<G, NT> st;
+  MfmaSoftmax<NT> st;
   st.init();
-  float* pwv = pw[wave];
   {
-    const int co = lane & 15, tp = lane >> 4;
-    uint2 R[kGroups], S8;
-    uint4 Vr[4];
-    auto load_block = [&](int j) {
+    // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes)
+    const size_t v_lane = (size_t)((4 * wave + ks) * kHeadDim + 8 * col) * 4;
+    auto load_block = [&](int j, RefineRegs& x) {
       const size_t bi = bi0 + j;
-      load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, R, S8);
-      const uint16_t* vb = p.v + ((head * p.L_cap + (size_t)(blk0 + j) * 64 + 16 * wave + tp) * kHeadDim + 8 * co);
+      load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, x.R, x.S8);
+      const uint4* vb = reinterpret_cast<const uint4*>(p.v + (head * p.L_cap + (size_t)(blk0 + j) * 64) * kHeadDim +
+                                                       v_lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
+      for (int q = 0; q < 4; ++q) x.V[q] = vb[q];
     };
-    if (K > 0) load_block(klist[0]);
-    for (int kk = 0; kk < K; ++kk) {
-      const int j = klist[kk];
+    auto refine = [&](int j, const RefineRegs& x) {
       const int n_rows = min(16, L - ((blk0 + j) * 64 + 16 * wave));
-      uint2 Rc[kGroups];
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) Rc[g] = R[g];
-      const uint2 S8c = S8;
-      uint4 Vc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Vc[i] = Vr[i];
-      if (kk + 1 < K) load_block(klist[kk + 1]);
-      if (n_rows <= 0) continue;  // this wave's tile lies past the sequence end
-
+      if (n_rows <= 0) return;  // this wave's tile lies past the sequence end
       float r[NT][4];
-      qf.residual(Rc, S8c, p.sm_scale, r);
-      float alpha_l[NT];
+      qf.residual(x.R, x.S8, p.sm_scale, r);
+      float s[NT][4];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int h = 4 * nt + hc;
         const int hh = h < G ? h : 0;
-        const float4 e4 = *reinterpret_cast<const float4*>(&u.est[j][wave][hh][4 * ks]);
+        const float4 e4 = *reinterpret_cast<const float4*>(&est[((j * kWaves + wave) * G + hh) * 16 + 4 * ks]);
         const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-        float s[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = (4 * ks + i < n_rows) ? fmaf(ev[i], scale4, r[nt][i]) : -INFINITY;
-        alpha_l[nt] = st.fold(nt, s, pwv, PG, hh, gc == 0 && h < G, ks);
+        for (int i = 0; i < 4; ++i) s[nt][i] = (4 * ks + i < n_rows) ? fmaf(ev[i], scale4, r[nt][i]) : -INFINITY;
       }
-      float alpha[G];
+      uint4 V[4] = {x.V[0], x.V[1], x.V[2], x.V[3]};
+      if (n_rows < 16) {  // zero the values of rows past the end (they may hold any bytes)
+        const int r0 = 4 * ks;
+        const uint32_t m01 = (r0 < n_rows ? 0xffffu : 0u) | (r0 + 1 < n_rows ? 0xffff0000u : 0u);
+        const uint32_t m23 = (r0 + 2 < n_rows ? 0xffffu : 0u) | (r0 + 3 < n_rows ? 0xffff0000u : 0u);
 #pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = uniform_lane(alpha_l[h >> 2], 4 * (h & 3));
-      st.template pv<PG>(alpha, Vc, pwv, lane, n_rows);
+        for (int q = 0; q < 4; ++q) {
+          V[q].x &= m01;
+          V[q].y &= m23;
+          V[q].z &= m01;
+          V[q].w &= m23;
+        }
+      }
+      h4 va[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        va[2 * q] = __builtin_bit_cast(h4, make_uint2(V[q].x, V[q].y));
+        va[2 * q + 1] = __builtin_bit_cast(h4, make_uint2(V[q].z, V[q].w));
+      }
+      st.step(s, va);
+    };
+    RefineRegs X, Y;
+    if (K > 0) load_block(klist[0], X);
+    for (int kk = 0; kk < K; kk += 2) {
+      if (kk + 1 < K) load_block(klist[kk + 1], Y);
+      refine(klist[kk], X);
+      if (kk + 1 >= K) break;
+      if (kk + 2 < K) load_block(klist[kk + 2], X);
+      refine(klist[kk + 1], Y);
     }
   }
   __syncthreads();  // est is no longer read: its LDS is reused by the combine
-
-  float hm[NT], hl[NT];
-  int hidx[NT];
-  bool hw[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    hm[nt] = st.m[nt];
-    hl[nt] = st.l[nt];
-    hidx[nt] = 4 * nt + hc < G ? 4 * nt + hc : 0;
-    hw[nt] = (lane < 16) && (gc == 0) && (4 * nt + hc < G);
-  }
-  finish_chunk<G, NT>(p, u.cl, st.acc, wave, lane, tid, b, hkv, chunk, hm, hl, hidx, hw);
+  st.template store<G>(cl, wave, lane);
+  __syncthreads();
+  combine_chunk<G>(p, cl, tid, b, hkv, chunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -748,7 +863,8 @@ static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL(pseudomax_kernel<G>, dim3(p.npart, p.Hkv, p.B), dim3(256), 0, s, p);
   if (stages & 2) {
     if (p.ev_start) (void)hipEventRecord(p.ev_start, s);
-    hipLaunchKernelGGL(attend_kernel<G>, dim3(p.nchunk, p.Hkv, p.B), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attend_kernel<G>, dim3(p.nchunk, p.Hkv, p.B), dim3(256), AttendCfg<G>::lds_bytes(p.cb), s,
+                       p);
     if (p.ev_stop) (void)hipEventRecord(p.ev_stop, s);
   }
   if (stages & 4) hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);

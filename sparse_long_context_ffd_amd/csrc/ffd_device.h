@@ -15,6 +15,7 @@ constexpr int kCodesBytes = 2048;       // per 64-token block and head
 constexpr int kSzBytes = 1024;
 constexpr int kResBytes = 8192;
 constexpr int kRscBytes = 512;
+constexpr int kVBytes = 16384;          // fp16 V of one 64-token block, token-quad tiled
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));

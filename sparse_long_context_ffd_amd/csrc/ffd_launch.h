@@ -13,7 +13,7 @@ struct DecodeParams {
   const int8_t* res;
   const uint8_t* rsc;
   const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
-  const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]
+  const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]: token-quad tiled (FFD), natural (dense)
   const int32_t* seq_lens; // [B]
   float* pmax;             // [B][npart][Hq] partial pseudo-maxima
   float* part_o;           // [B][Hq][nchunk][128]
@@ -31,6 +31,8 @@ struct DecodeParams {
 
 hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, int t_end, void* codes,
                        void* sz, void* res, void* rsc, hipStream_t stream);
+hipError_t launch_pack_v(const void* v, int B, int Hkv, int L_cap, int t_begin, int t_end, void* vt,
+                         hipStream_t stream);
 hipError_t launch_ffd_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_dense_decode(const DecodeParams& p, hipStream_t s);
 

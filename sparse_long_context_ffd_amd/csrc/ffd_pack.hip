@@ -148,6 +148,55 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   *reinterpret_cast<uint16_t*>(sbase + rsc_off(tb, g)) = s8b;
 }
 
+// V pack: natural fp16 rows -> the token-quad tiled layout the refine's
+// P.V MFMA reads (element ((t/4)*128 + ch)*4 + t%4 of the head's array), so a
+// lane's A fragment (4 tokens of one channel) is 8 contiguous bytes.  Thread =
+// (token quad, channel pair): 4 quads x 64 pairs per work-group.  A quad
+// entirely inside [t_begin, t_end) is stored with one 16-byte write; the
+// partial quads at the ends of the range store only their in-range tokens.
+__global__ __launch_bounds__(256) void pack_v_kernel(const uint16_t* __restrict__ v, int L_cap, int t_begin,
+                                                     int t_end, uint16_t* __restrict__ vt) {
+  const int tid = threadIdx.x;
+  const int cp = tid & 63;
+  const int tq = (t_begin >> 2) + blockIdx.x * 4 + (tid >> 6);
+  const size_t head = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int t0 = 4 * tq;
+  if (t0 >= t_end) return;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + j;
+    const bool in = t >= t_begin && t < t_end;
+    w[j] = in ? *reinterpret_cast<const uint32_t*>(v + (head * L_cap + t) * kHeadDim + 2 * cp) : 0u;
+  }
+  // channel 2cp: low halves of w[0..3]; channel 2cp+1: high halves
+  const uint32_t a0 = (w[0] & 0xffffu) | (w[1] << 16), a1 = (w[2] & 0xffffu) | (w[3] << 16);
+  const uint32_t b0 = (w[0] >> 16) | (w[1] & 0xffff0000u), b1 = (w[2] >> 16) | (w[3] & 0xffff0000u);
+  uint16_t* dst = vt + (head * L_cap + (size_t)t0) * kHeadDim + 8 * cp;
+  if (t0 >= t_begin && t0 + 4 <= t_end) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(a0, a1, b0, b1);
+  } else {
+    const uint32_t lo[4] = {a0 & 0xffffu, a0 >> 16, a1 & 0xffffu, a1 >> 16};
+    const uint32_t hi[4] = {b0 & 0xffffu, b0 >> 16, b1 & 0xffffu, b1 >> 16};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (t0 + j >= t_begin && t0 + j < t_end) {
+        dst[j] = (uint16_t)lo[j];
+        dst[4 + j] = (uint16_t)hi[j];
+      }
+  }
+}
+
+hipError_t launch_pack_v(const void* v, int B, int Hkv, int L_cap, int t_begin, int t_end, void* vt,
+                         hipStream_t stream) {
+  const int nq = (t_end + 3) / 4 - t_begin / 4;
+  if (t_end <= t_begin || nq <= 0) return hipSuccess;
+  dim3 grid((nq + 3) / 4, Hkv, B);
+  hipLaunchKernelGGL(pack_v_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(v), L_cap, t_begin,
+                     t_end, static_cast<uint16_t*>(vt));
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, int t_end, void* codes,
                        void* sz, void* res, void* rsc, hipStream_t stream) {
   const int n = t_end - t_begin;

@@ -47,11 +47,15 @@ def shape_for(w, chunk_blocks=0, sink=None, local=None):
                           local=w.local if local is None else local, chunk_blocks=chunk_blocks)
 
 
-def gpu_pack(shape, k_dev, fill=0xFF, t_begin=0, t_end=None):
-    """Pack [t_begin, t_end) into a fresh cache whose bytes start as `fill`."""
+def gpu_pack(shape, k_dev, v_dev=None, fill=0xFF, t_begin=0, t_end=None):
+    """Pack K (and V, when given) tokens [t_begin, t_end) into a fresh cache
+    whose bytes start as `fill`."""
     import sparse_long_context_ffd_amd as ffd
     cache = ffd.PackedCache(shape).fill_(fill)
-    ffd.quantize_k(shape, k_dev, t_begin, shape.max_seq_len if t_end is None else t_end, cache)
+    t_end = shape.max_seq_len if t_end is None else t_end
+    ffd.quantize_k(shape, k_dev, t_begin, t_end, cache)
+    if v_dev is not None:
+        ffd.pack_v(shape, v_dev, t_begin, t_end, cache)
     return cache
 
 
@@ -61,7 +65,7 @@ def decode_cache_fields(cache, w):
 
 
 def cache_to_host(cache):
-    return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale")}
+    return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
 def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE):

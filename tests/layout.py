@@ -48,10 +48,23 @@ _RES = _res_map()
 _RSC = (np.arange(4)[None, :] * 64 + np.arange(64)[:, None])      # [t][g] -> element g*64 + t
 
 
+def _v_map(L_cap: int):
+    """[t][ch] -> fp16 element index of the token-quad tiled V of one head."""
+    t = np.arange(L_cap)[:, None]
+    ch = np.arange(128)[None, :]
+    return ((t // 4) * 128 + ch) * 4 + t % 4
+
+
+def decode_v(v: np.ndarray, B: int, Hkv: int, L_cap: int) -> np.ndarray:
+    """Tiled V bytes -> fp16 [B][Hkv][L_cap][128]."""
+    return v.view(np.float16).reshape(B, Hkv, L_cap * 128)[..., _v_map(L_cap)]
+
+
 def decode_cache(codes: np.ndarray, sz: np.ndarray, res: np.ndarray, rscale: np.ndarray,
-                 B: int, Hkv: int, L_cap: int):
+                 B: int, Hkv: int, L_cap: int, v: np.ndarray = None):
     """Byte buffers (uint8, as copied from the GPU) -> dict of logical fields
-    shaped like ``quantize_k`` output over [B][Hkv][L_cap]."""
+    shaped like ``quantize_k`` output over [B][Hkv][L_cap] (plus "v" when the
+    tiled V bytes are given)."""
     nb = L_cap // 64
     words = codes.view(np.uint32).reshape(B, Hkv, nb, 512)
     c = (words[..., _WORD] >> _BIT.astype(np.uint32)) & 3                     # [B,Hkv,nb,64,128]
@@ -60,7 +73,9 @@ def decode_cache(codes: np.ndarray, sz: np.ndarray, res: np.ndarray, rscale: np.
     zero = h[..., _SZ + 1]
     r = res.view(np.int8).reshape(B, Hkv, nb, 8192)[..., _RES]
     s8 = rscale.view(np.float16).reshape(B, Hkv, nb, 256)[..., _RSC]
+    out = {} if v is None else {"v": decode_v(v, B, Hkv, L_cap)}
     return {
+        **out,
         "codes": c.astype(np.uint8).reshape(B, Hkv, L_cap, 128),
         "scale": scale.reshape(B, Hkv, L_cap, 4),
         "zero": zero.reshape(B, Hkv, L_cap, 4),

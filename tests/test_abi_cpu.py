@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 100
+    assert L.ffd_version() == 200
 
 
 def test_strerror_covers_codes():
@@ -110,15 +110,28 @@ def test_dense_and_pack_argument_errors():
     assert L.ffd_quantize_k(ctypes.byref(s), FAKE + 6, 0, 5, ctypes.byref(c), None) == -3
     assert L.ffd_quantize_k(ctypes.byref(s), FAKE, 0, 5, ctypes.byref(_lib.Cache(FAKE, None, FAKE, FAKE, None)),
                             None) == -1
+    cv = _lib.Cache(None, None, None, None, FAKE)      # ffd_pack_v reads only cache->v
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, -1, 5, ctypes.byref(cv), None) == -6
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, 6, 5, ctypes.byref(cv), None) == -6
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, 0, 4097, ctypes.byref(cv), None) == -6
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, 7, 7, ctypes.byref(cv), None) == 0
+    assert L.ffd_pack_v(ctypes.byref(s), None, 0, 5, ctypes.byref(cv), None) == -1
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, 0, 5, ctypes.byref(_lib.Cache(FAKE, FAKE, FAKE, FAKE, None)),
+                        None) == -1
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE + 2, 0, 5, ctypes.byref(cv), None) == -3
+    assert L.ffd_pack_v(ctypes.byref(s), FAKE, 0, 5, ctypes.byref(_lib.Cache(None, None, None, None, FAKE + 8)),
+                        None) == -3
 
 
 def test_cache_and_workspace_sizes():
     s = ffd.make_shape(2, 28, 4, 32768)
     nb = ffd.cache_bytes(s)
     blocks = 2 * 4 * 512
-    assert nb == {"codes": blocks * 2048, "sz": blocks * 1024, "res": blocks * 8192, "rscale": blocks * 512}
+    assert nb == {"codes": blocks * 2048, "sz": blocks * 1024, "res": blocks * 8192, "rscale": blocks * 512,
+                  "v": blocks * 16384}
     per_token = sum(nb.values()) / (2 * 4 * 32768)
-    assert per_token == 184          # 2-bit codes 32 + (scale, zero) 16 + int8 residual 128 + rscale 8
+    # 2-bit codes 32 + (scale, zero) 16 + int8 residual 128 + rscale 8 + fp16 V 256
+    assert per_token == 440
     cb, nch = ffd.plan(s)
     assert nch == math.ceil(512 / cb)
     rows = 2 * 28

@@ -24,8 +24,7 @@ def _run(w, seed, deltas, heads=None, chunk_blocks=0, sink=None, local=None, fil
     W = w.local if local is None else local
     qd, kd, vd = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
     ld = dev(c["seq_lens"], torch)
-    cache = gpu_pack(shape, kd, fill=fill)
-    cache.v = vd
+    cache = gpu_pack(shape, kd, vd, fill=fill)
     G = w.group
     todo = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
     stats = []
@@ -112,8 +111,7 @@ def test_infinite_delta_equals_dense_over_khat():
     w = WORKLOADS["tiny_h4x1_4k"]
     c = make_case(w, 0)
     shape = shape_for(w)
-    cache = gpu_pack(shape, dev(c["k"], torch))
-    cache.v = dev(c["v"], torch)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
     got = gpu_decode(shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), math.inf, torch)
     assert (got["keep"][0, 0, :64] == 1).all()
     _, khat = orc.dequantize(orc.quantize_k(c["k"][0, 0]))
@@ -143,8 +141,7 @@ def test_graph_replay_matches_eager():
     c = make_case(w, 1)
     shape = shape_for(w)
     q, lens = dev(c["q"], torch), dev(c["seq_lens"], torch)
-    cache = gpu_pack(shape, dev(c["k"], torch))
-    cache.v = dev(c["v"], torch)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
     ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     out_e = torch.empty((1, 4, 128), dtype=torch.float16, device="cuda")
     ffd.decode_attn(shape, q, cache, lens, 5.0, SM_SCALE, out_e, ws)

@@ -107,3 +107,38 @@ def test_pack_token_range_leaves_other_bytes_untouched():
             if a.dtype == np.float16:
                 a, u = a.view(np.uint16), u.view(np.uint16)
             assert (a[:, :, ~sel] == u[:, :, ~sel]).all(), f"range [{t0},{t1}) touched other tokens in {f}"
+
+
+@pytest.mark.parametrize("name,heads", [("tiny_h4x1_4k", None), ("qwen7b_b16_16k32k", [(3, 2), (15, 0)])])
+def test_pack_v_tiled_bit_exact(name, heads):
+    """ffd_pack_v moves every fp16 value unchanged into the token-quad tiled layout."""
+    torch = torch_mod()
+    w = WORKLOADS[name]
+    say(f"pack_v {name} heads={heads}")
+    c = make_case(w, 0, heads=heads)
+    shape = shape_for(w)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
+    got = decode_cache(**cache_to_host(cache), B=w.batch, Hkv=w.kv_heads, L_cap=w.max_len)["v"]
+    for b, h in heads or [(0, 0)]:
+        assert np.array_equal(got[b, h].view(np.uint16), c["v"][b, h].view(np.uint16)), f"{name} b{b} h{h}"
+
+
+def test_pack_v_token_range_leaves_other_bytes_untouched():
+    """Ranges that start or end inside a 4-token quad write exactly their tokens."""
+    torch = torch_mod()
+    rng = np.random.default_rng(5)
+    L_cap = 512
+    v = rng.standard_normal((2, 2, L_cap, 128)).astype(np.float16)
+    k = np.zeros_like(v)
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(2, 4, 2, L_cap)
+    kd, vd = dev(k, torch), dev(v, torch)
+    for (t0, t1) in [(100, 101), (63, 200), (0, 1), (511, 512), (130, 130), (2, 7), (5, 6), (0, 512)]:
+        say(f"pack_v range [{t0},{t1})")
+        cache = ffd.PackedCache(shape).fill_(0xAB)
+        ffd.pack_v(shape, vd, t0, t1, cache)
+        got = decode_cache(**cache_to_host(cache), B=2, Hkv=2, L_cap=L_cap)["v"].view(np.uint16)
+        sel = np.zeros(L_cap, bool)
+        sel[t0:t1] = True
+        assert (got[:, :, sel] == v.view(np.uint16)[:, :, sel]).all(), f"range [{t0},{t1})"
+        assert (got[:, :, ~sel] == 0xABAB).all(), f"range [{t0},{t1}) touched other tokens"
