@@ -16,10 +16,11 @@
 // rows.  The B operand holds q with column n = 4*h + g carrying head h
 // restricted to 32-channel group g (zero elsewhere), so one accumulator
 // collects per-(head, group) dot products whose fp32 epilogue applies that
-// token-group's scale; a quad sum over g finishes the dot product.
-//   thumbnail: A = 1 + c/4 (exact fp16), accumulator starts at -sum_g(q):
-//              C = (q_g . c_g)/4;  est = 4*scale*C + zero*sum_g(q)
-//   residual:  A = 384 + e (exact fp16), accumulator starts at -384*sum_g(q):
+// token-group's scale; a quad sum over g finishes the dot product.  Scores
+// are kept as raw dot products x = q . k (s = sm_scale * x):
+//   thumbnail: A = 4 + c (exact fp16), accumulator starts at -4*sum_g(q):
+//              C = q_g . c_g;      est = scale*C + zero*sum_g(q)
+//   residual:  A = 1152 + e (exact fp16), accumulator starts at -1152*sum_g(q):
 //              C = q_g . e_g;      exact = est + rscale*C
 //
 // Work decomposition of attend/dense: one work-group (4 wave64) per chunk of `cb`
@@ -33,6 +34,8 @@
 namespace ffd {
 
 constexpr int kWaves = 4;
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited on
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ inline int clamp_len(const DecodeParams& p, int b) {
   const int L = p.seq_lens[b];
@@ -46,35 +49,37 @@ __device__ inline float quad_sum(float v) {
   return v;
 }
 
-// 2-bit code word -> MFMA A fragment of 8 fp16 values 1 + c/4 (channels j = 0..7)
-constexpr uint32_t kCodeMask = 0x03000300u, kOneHalf2 = 0x3C003C00u;
-__device__ inline h8 unpack_even(uint32_t w, uint32_t one) {
+// 2-bit code word -> MFMA A fragment of 8 fp16 values 4 + c (channels j = 0..7):
+// the code lands in mantissa bits 8-9 of an fp16 with exponent 2 (ulp 1/4)
+constexpr uint32_t kCodeMask = 0x03000300u, kOneHalf2 = 0x44004400u;
+// (`mask` = kCodeMask in an SGPR, `one` = kOneHalf2 in a VGPR)
+__device__ inline h8 unpack_even(uint32_t w, uint32_t mask, uint32_t one) {
   uint4 d;
-  d.x = and_or(w, kCodeMask, one);
-  d.y = and_or(w >> 2, kCodeMask, one);
-  d.z = and_or(w >> 4, kCodeMask, one);
-  d.w = and_or(w >> 6, kCodeMask, one);
+  d.x = and_or(w, mask, one);
+  d.y = and_or(w >> 2, mask, one);
+  d.z = and_or(w >> 4, mask, one);
+  d.w = and_or(w >> 6, mask, one);
   return __builtin_bit_cast(h8, d);
 }
-__device__ inline h8 unpack_odd(uint32_t w, uint32_t one) {
+__device__ inline h8 unpack_odd(uint32_t w, uint32_t mask, uint32_t one) {
   uint4 d;
-  d.x = and_or(w << 8, kCodeMask, one);
-  d.y = and_or(w << 6, kCodeMask, one);
-  d.z = and_or(w << 4, kCodeMask, one);
-  d.w = and_or(w << 2, kCodeMask, one);
+  d.x = and_or(w << 8, mask, one);
+  d.y = and_or(w << 6, mask, one);
+  d.z = and_or(w << 4, mask, one);
+  d.w = and_or(w << 2, mask, one);
   return __builtin_bit_cast(h8, d);
 }
-// 8 int8 residuals -> MFMA A fragment of fp16 values 384 + e (exact)
-__device__ inline uint32_t res_pair(uint32_t x, uint32_t sel) {
-  return (__builtin_amdgcn_perm(x, x, sel) << 2) | 0x5C005C00u;
-}
+// 8 int8 residuals -> MFMA A fragment of fp16 values 1152 + e (exact): after
+// the XOR each byte is e + 128, and one byte permute places two of them as the
+// low mantissa bytes of fp16 values with high byte 0x64 (1024 + byte)
+constexpr uint32_t kResHigh = 0x64646464u;
 __device__ inline h8 unpack_res(uint2 r) {
-  const uint32_t x = r.x ^ 0x80808080u, y = r.y ^ 0x80808080u;  // offset binary e + 128
+  const uint32_t x = r.x ^ 0x80808080u, y = r.y ^ 0x80808080u;
   uint4 d;
-  d.x = res_pair(x, 0x0C010C00u);
-  d.y = res_pair(x, 0x0C030C02u);
-  d.z = res_pair(y, 0x0C010C00u);
-  d.w = res_pair(y, 0x0C030C02u);
+  d.x = __builtin_amdgcn_perm(kResHigh, x, 0x04010400u);
+  d.y = __builtin_amdgcn_perm(kResHigh, x, 0x04030402u);
+  d.z = __builtin_amdgcn_perm(kResHigh, y, 0x04010400u);
+  d.w = __builtin_amdgcn_perm(kResHigh, y, 0x04030402u);
   return __builtin_bit_cast(h8, d);
 }
 
@@ -87,11 +92,14 @@ template <int G>
 struct QFrags {
   static constexpr int NT = (G + 3) / 4;  // 16-column tiles (4 heads x 4 groups each)
   h8 B[NT][kGroups];
-  float c_est[NT], c_res[NT], qq[NT];
+  float c_est[NT], c_res[NT], qq[NT];  // accumulator starts; qq = sum_g(q) of the lane's column
+  uint32_t code_mask, code_one;        // kCodeMask (SGPR), kOneHalf2 (VGPR)
 
   // q2: q as fp16 pairs [G][64]; qg: per-(head, group) sums of q
   __device__ void build(const h2 (*q2)[64], const float (*qg)[kGroups], int lane) {
     const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+    code_one = opaque_vgpr(kOneHalf2);
+    code_mask = __builtin_amdgcn_readfirstlane(opaque_vgpr(kCodeMask));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int h = 4 * nt + hc;
@@ -109,19 +117,18 @@ struct QFrags {
         B[nt][g] = f;
       }
       const float Q = live ? qg[h][gc] : 0.f;
-      c_est[nt] = -Q;
-      c_res[nt] = -384.f * Q;
-      qq[nt] = 0.25f * Q;
+      c_est[nt] = -4.f * Q;
+      c_res[nt] = -1152.f * Q;
+      qq[nt] = Q;
     }
   }
 
-  // estimated scores of the lane's 4 C rows divided by 4*sm_scale; cw = codes
-  // words (groups 0,1 | 2,3) of the lane's A row, zw = (scale, zero) of the
-  // lane's 4 C rows for group gc
+  // estimated dot products q . (zero + c*scale) of the lane's 4 C rows; cw =
+  // codes words (groups 0,1 | 2,3) of the lane's A row, zw = (scale, zero) of
+  // the lane's 4 C rows for group gc
   __device__ void estimate(uint2 cw, uint4 zw, float (&e)[NT][4]) const {
-    const uint32_t one = kOneHalf2;
-    const h8 a0 = unpack_even(cw.x, one), a1 = unpack_odd(cw.x, one);
-    const h8 a2 = unpack_even(cw.y, one), a3 = unpack_odd(cw.y, one);
+    const h8 a0 = unpack_even(cw.x, code_mask, code_one), a1 = unpack_odd(cw.x, code_mask, code_one);
+    const h8 a2 = unpack_even(cw.y, code_mask, code_one), a3 = unpack_odd(cw.y, code_mask, code_one);
     const uint32_t zs[4] = {zw.x, zw.y, zw.z, zw.w};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -135,12 +142,12 @@ struct QFrags {
     }
   }
 
-  // residual term sm_scale * sum_g rscale_g * (q_g . e_g) of the lane's 4 C
-  // rows; R[g] = residual bytes of the lane's A row for group g, S8 = rscale
-  // of the lane's 4 C rows for group gc
-  __device__ void residual(const uint2 (&R)[kGroups], uint2 S8, float sm_scale, float (&r)[NT][4]) const {
+  // residual dot products sum_g rscale_g * (q_g . e_g) of the lane's 4 C rows;
+  // R[g] = residual bytes of the lane's A row for group g, S8 = rscale of the
+  // lane's 4 C rows for group gc
+  __device__ void residual(const uint2 (&R)[kGroups], uint2 S8, float (&r)[NT][4]) const {
     const h8 a0 = unpack_res(R[0]), a1 = unpack_res(R[1]), a2 = unpack_res(R[2]), a3 = unpack_res(R[3]);
-    const float s8[4] = {lo_h(S8.x), hi_h(S8.x), lo_h(S8.y), hi_h(S8.y)};
+    const uint32_t s8[4] = {S8.x, S8.x >> 16, S8.y, S8.y >> 16};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       f4 c = {c_res[nt], c_res[nt], c_res[nt], c_res[nt]};
@@ -149,7 +156,7 @@ struct QFrags {
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a2, B[nt][2], c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a3, B[nt][3], c, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[nt][i] = quad_sum(s8[i] * c[i]) * sm_scale;
+      for (int i = 0; i < 4; ++i) r[nt][i] = quad_sum(fmaf(lo_h(s8[i]), c[i], 0.f));
     }
   }
 };
@@ -231,8 +238,7 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   qf.build(q2, qg, lane);
   float e[NT][4], r[NT][4];
   qf.estimate(cw, zw, e);
-  qf.residual(R, S8, p.sm_scale, r);
-  const float scale4 = 4.f * p.sm_scale;
+  qf.residual(R, S8, r);
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) {
       const int t = blk_c * 64 + 16 * wave + 4 * ks + i;
       const bool sup = live && t < L && (t < s_end || t >= l_beg);
-      mx = fmaxf(mx, sup ? fmaf(e[nt][i], scale4, r[nt][i]) : -INFINITY);
+      mx = fmaxf(mx, sup ? (e[nt][i] + r[nt][i]) * p.sm_scale : -INFINITY);
     }
     mx = rows_max(mx);
     const int h = 4 * nt + hc;
@@ -418,32 +424,38 @@ struct MfmaSoftmax {
       for (int jm = 0; jm < 8; ++jm) o[n][jm] = f4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  // fold one tile: s = scores of the lane's 4 rows per column tile (rows past
-  // the sequence end -inf), va = V^T fragments (rows past the end zeroed)
-  __device__ void step(const float (&s)[NT][4], const h4 (&va)[8]) {
+  // fold one tile.  x = raw dot products q.k of the lane's 4 rows per column
+  // tile (rows past the sequence end -inf), c2 = sm_scale * log2(e), va = V^T
+  // fragments (rows past the end zeroed).  The reference max m moves only when
+  // a tile's max exceeds it by more than `slack` (8 / c2: weights stay below
+  // 2^8), so most tiles skip the rescale of the accumulators.
+  __device__ void step(const float (&x)[NT][4], float c2, float slack, const h4 (&va)[8]) {
     float alpha[NT];
     h4 bhi[NT], blo[NT];
     bool moved = false;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const float tm = rows_max(fmaxf(fmaxf(s[n][0], s[n][1]), fmaxf(s[n][2], s[n][3])));
-      const float mn = fmaxf(m[n], tm);
-      const float mr = mn == -INFINITY ? 0.f : mn;
-      alpha[n] = __builtin_amdgcn_exp2f((m[n] - mr) * kLog2e);
+      const float tm = rows_max(fmaxf(fmaxf(x[n][0], x[n][1]), fmaxf(x[n][2], x[n][3])));
+      const bool mv = tm > m[n] + slack;
+      const float mn = mv ? tm : m[n];
+      alpha[n] = mv ? __builtin_amdgcn_exp2f((m[n] - mn) * c2) : 1.f;
+      moved = moved || mv;
+      const float off = mn == -INFINITY ? 0.f : -mn * c2;
       float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f((s[n][i] - mr) * kLog2e);
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[n][i], c2, off));
       l[n] = fmaf(l[n], alpha[n], rows_sum((pr[0] + pr[1]) + (pr[2] + pr[3])));
       m[n] = mn;
-      moved = moved || (alpha[n] != 1.f);
       const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[0], pr[1]));
       const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2], pr[3]));
-      const h2 l01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[0] - (float)h01.x, pr[1] - (float)h01.y));
-      const h2 l23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pr[2] - (float)h23.x, pr[3] - (float)h23.y));
+      const h2 l01 = __builtin_bit_cast(
+          h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-(float)h01.x, 1.f, pr[0]), fmaf(-(float)h01.y, 1.f, pr[1])));
+      const h2 l23 = __builtin_bit_cast(
+          h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-(float)h23.x, 1.f, pr[2]), fmaf(-(float)h23.y, 1.f, pr[3])));
       bhi[n] = h4{h01.x, h01.y, h23.x, h23.y};
       blo[n] = h4{l01.x, l01.y, l23.x, l23.y};
     }
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // rescale only when some head's max moved
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -457,10 +469,11 @@ struct MfmaSoftmax {
         o[n][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], blo[n], o[n][jm], 0, 0, 0);
       }
   }
-  // store the wave's state for the combine: lanes of group column 0 of each
-  // live head write its 128 channels (32 per row group ks) and m, l
+  // store the wave's state for the combine (m converted to a softmax logit):
+  // lanes of group column 0 of each live head write its 128 channels (32 per
+  // row group ks) and m, l
   template <int G>
-  __device__ void store(CombineLds<G>& cl, int wave, int lane) const {
+  __device__ void store(CombineLds<G>& cl, int wave, int lane, float sm_scale) const {
     const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -473,7 +486,7 @@ struct MfmaSoftmax {
           *reinterpret_cast<float4*>(dst + 4) = make_float4(o[n][4][i], o[n][5][i], o[n][6][i], o[n][7][i]);
         }
         if (ks == 0) {
-          cl.m[wave][h] = m[n];
+          cl.m[wave][h] = m[n] * sm_scale;
           cl.l[wave][h] = l[n];
         }
       }
@@ -569,12 +582,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __syncthreads();
   QFrags<G> qf;
   qf.build(q2, qg, lane);
-  const float scale4 = 4.f * p.sm_scale;
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+  // Drain every load issued so far (first batch, q, the pseudo-max parts of a
+  // runtime-length loop) so that the pipelined scan below starts from an exact
+  // count of loads in flight.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
-  // estimates are kept divided by 4*sm_scale; rows past the sequence end (only
-  // in the last block) are set to -inf
+  // estimates are kept as dot products (logit / sm_scale); rows past the
+  // sequence end (only in the last block) are set to -inf
   auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint4 (&zw)[4]) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -602,11 +618,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       }
     }
   };
+  // The next batch is loaded unconditionally (indices clamped to the chunk, so
+  // a batch past the end re-reads the last block from L2): every path then
+  // issues the same number of loads, which lets the compiler's load counters
+  // wait for the batch being scanned only, not for the one in flight.
   for (int j0 = 0; j0 < nbl; j0 += 8) {
-    if (j0 + 4 < nbl) load_batch(j0 + 4, cwB, zwB);
+    load_batch(j0 + 4, cwB, zwB);
     scan_batch(j0, cwA, zwA);
     if (j0 + 4 >= nbl) break;
-    if (j0 + 8 < nbl) load_batch(j0 + 8, cwA, zwA);
+    load_batch(j0 + 8, cwA, zwA);
     scan_batch(j0 + 4, cwB, zwB);
   }
   __syncthreads();
@@ -625,7 +645,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         float bm = tm[0];
 #pragma unroll
         for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tm[r * G]);
-        bm *= scale4;
+        bm *= p.sm_scale;
         kp = kp || (bm >= thr_s[h]);
         if (p.dbg_bmax) p.dbg_bmax[((size_t)b * p.Hq + qh0 + h) * p.nblk_cap + blk] = bm;
       }
@@ -652,54 +672,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
       for (int q = 0; q < 4; ++q) x.V[q] = vb[q];
     };
-    auto refine = [&](int j, const RefineRegs& x) {
+    const float c2 = p.sm_scale * kLog2e, slack = 8.f / c2;
+    auto refine = [&](int j, RefineRegs& x) {
       const int n_rows = min(16, L - ((blk0 + j) * 64 + 16 * wave));
       if (n_rows <= 0) return;  // this wave's tile lies past the sequence end
-      float r[NT][4];
-      qf.residual(x.R, x.S8, p.sm_scale, r);
-      float s[NT][4];
+      float xs[NT][4];
+      qf.residual(x.R, x.S8, xs);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int h = 4 * nt + hc;
         const int hh = h < G ? h : 0;
         const float4 e4 = *reinterpret_cast<const float4*>(&est[((j * kWaves + wave) * G + hh) * 16 + 4 * ks]);
-        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[nt][i] = (4 * ks + i < n_rows) ? fmaf(ev[i], scale4, r[nt][i]) : -INFINITY;
+        xs[nt][0] += e4.x;
+        xs[nt][1] += e4.y;
+        xs[nt][2] += e4.z;
+        xs[nt][3] += e4.w;
       }
-      uint4 V[4] = {x.V[0], x.V[1], x.V[2], x.V[3]};
-      if (n_rows < 16) {  // zero the values of rows past the end (they may hold any bytes)
+      if (n_rows < 16) {  // rows past the end: -inf scores, zero values (their bytes may be anything)
         const int r0 = 4 * ks;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xs[nt][i] = r0 + i < n_rows ? xs[nt][i] : -INFINITY;
         const uint32_t m01 = (r0 < n_rows ? 0xffffu : 0u) | (r0 + 1 < n_rows ? 0xffff0000u : 0u);
         const uint32_t m23 = (r0 + 2 < n_rows ? 0xffffu : 0u) | (r0 + 3 < n_rows ? 0xffff0000u : 0u);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          V[q].x &= m01;
-          V[q].y &= m23;
-          V[q].z &= m01;
-          V[q].w &= m23;
+          x.V[q].x &= m01;
+          x.V[q].y &= m23;
+          x.V[q].z &= m01;
+          x.V[q].w &= m23;
         }
       }
       h4 va[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        va[2 * q] = __builtin_bit_cast(h4, make_uint2(V[q].x, V[q].y));
-        va[2 * q + 1] = __builtin_bit_cast(h4, make_uint2(V[q].z, V[q].w));
+        va[2 * q] = __builtin_bit_cast(h4, make_uint2(x.V[q].x, x.V[q].y));
+        va[2 * q + 1] = __builtin_bit_cast(h4, make_uint2(x.V[q].z, x.V[q].w));
       }
-      st.step(s, va);
+      st.step(xs, c2, slack, va);
     };
+    // next kept block loaded while the current one is computed; as in the
+    // scan, unconditionally (the last block is re-read past the end of the list)
     RefineRegs X, Y;
     if (K > 0) load_block(klist[0], X);
     for (int kk = 0; kk < K; kk += 2) {
-      if (kk + 1 < K) load_block(klist[kk + 1], Y);
+      load_block(klist[min(kk + 1, K - 1)], Y);
       refine(klist[kk], X);
       if (kk + 1 >= K) break;
-      if (kk + 2 < K) load_block(klist[kk + 2], X);
+      load_block(klist[min(kk + 2, K - 1)], X);
       refine(klist[kk + 1], Y);
     }
   }
   __syncthreads();  // est is no longer read: its LDS is reused by the combine
-  st.template store<G>(cl, wave, lane);
+  st.template store<G>(cl, wave, lane, p.sm_scale);
   __syncthreads();
   combine_chunk<G>(p, cl, tid, b, hkv, chunk);
 }

@@ -89,12 +89,17 @@ __device__ inline float rows_sum(float v) {
   return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
-// (x & mask) | bits in one VALU op (the compiler splits it into two)
-__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "s"(mask), "v"(bits));
-  return d;
+// A 32-bit constant in a VGPR whose value the compiler cannot see.  With the
+// mask in an SGPR and the constant in a VGPR, (x & mask) | bits is selected as
+// one v_and_or_b32 (with both as visible literals the compiler emits two
+// instructions); keeping the op itself in compiled code, not inline asm, lets
+// the compiler account for its wait states before an MFMA reads the result.
+__device__ inline uint32_t opaque_vgpr(uint32_t k) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1\n\ts_nop 1" : "=v"(r) : "s"(k));  // wait states cover any reader
+  return r;
 }
+__device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { return (x & mask) | bits; }
 
 // maximum over all 64 lanes, returned in every lane
 __device__ inline float wave_max(float v) {
