@@ -95,28 +95,58 @@ struct QFrags {
   float c_est[NT], c_res[NT], qq[NT];  // accumulator starts; qq = sum_g(q) of the lane's column
   uint32_t code_mask, code_one;        // kCodeMask (SGPR), kOneHalf2 (VGPR)
 
-  // q2: q as fp16 pairs [G][64]; qg: per-(head, group) sums of q
-  __device__ void build(const h2 (*q2)[64], const float (*qg)[kGroups], int lane) {
+  // q of the group's G heads ([G][128] fp16 at `qh`) is read once per
+  // work-group, one dword per thread, into `lds` ([G*64] dwords): every wave
+  // reading its own copy would send four times the requests to the few L2
+  // lines that all work-groups of a head share.  stage_load issues the
+  // global loads, stage_store writes them to LDS once they have landed.
+  static constexpr int kQPer = (G * 64 + 255) / 256;
+  struct Stage {
+    uint32_t w[kQPer];
+  };
+  __device__ static void stage_load(const uint16_t* qh, int tid, Stage& st) {
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = tid + 256 * k;
+      st.w[k] = i < G * 64 ? reinterpret_cast<const uint32_t*>(qh)[i] : 0u;
+    }
+  }
+  __device__ static void stage_store(const Stage& st, int tid, uint32_t* lds) {
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k)
+      if (tid + 256 * k < G * 64) lds[tid + 256 * k] = st.w[k];
+  }
+  // The lane's share of q (after a barrier): channels 32*gc + 8*ks .. +7 of
+  // head 4*nt + hc, the only nonzero part of its B fragments (zero for the
+  // padding heads of the last column tile)
+  struct Load {
+    uint4 v[NT];
+  };
+  __device__ static void load(const uint32_t* lds, int lane, Load& ql) {
     const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int h = 4 * nt + hc;
+      ql.v[nt] = make_uint4(0, 0, 0, 0);
+      if (h < G) ql.v[nt] = *reinterpret_cast<const uint4*>(lds + h * 64 + 16 * gc + 4 * ks);
+    }
+  }
+  // B fragments and per-(head, group) sums Q of q (sum over the four k-slice
+  // lanes of the column), once the loads have landed
+  __device__ void build(const Load& ql, int lane) {
+    const int gc = lane & 3;
     code_one = opaque_vgpr(kOneHalf2);
     code_mask = __builtin_amdgcn_readfirstlane(opaque_vgpr(kCodeMask));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int h = 4 * nt + hc;
-      const bool live = h < G;
+      const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        h8 f;
+      for (int g = 0; g < kGroups; ++g) B[nt][g] = __builtin_bit_cast(h8, g == gc ? ql.v[nt] : z);
+      const uint32_t w[4] = {ql.v[nt].x, ql.v[nt].y, ql.v[nt].z, ql.v[nt].w};
+      float part = 0.f;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          h2 pr = {(_Float16)0.f, (_Float16)0.f};
-          if (live && g == gc) pr = q2[h][16 * g + 4 * ks + d];
-          f[2 * d] = pr.x;
-          f[2 * d + 1] = pr.y;
-        }
-        B[nt][g] = f;
-      }
-      const float Q = live ? qg[h][gc] : 0.f;
+      for (int i = 0; i < 4; ++i) part += lo_h(w[i]) + hi_h(w[i]);
+      const float Q = rows_sum(part);
       c_est[nt] = -4.f * Q;
       c_res[nt] = -1152.f * Q;
       qq[nt] = Q;
@@ -180,23 +210,6 @@ __device__ inline void load_residual(const int8_t* rb, const uint8_t* sb, const 
   S8 = *reinterpret_cast<const uint2*>(sb + to.rsc);
 }
 
-// q of the group's heads into LDS as fp16 pairs, and per-(head, group) sums
-template <int G>
-__device__ inline void stage_q(const DecodeParams& p, int b, int qh0, int tid, h2 (*q2)[64]) {
-  for (int i = tid; i < G * 64; i += 256)
-    q2[i >> 6][i & 63] = __builtin_bit_cast(
-        h2, *reinterpret_cast<const uint32_t*>(p.q + ((size_t)b * p.Hq + qh0 + (i >> 6)) * kHeadDim + 2 * (i & 63)));
-}
-template <int G>
-__device__ inline void group_sums(const h2 (*q2)[64], float (*qg)[kGroups], int tid) {
-  if (tid < G * kGroups) {
-    const int h = tid >> 2, g = tid & 3;
-    float s = 0.f;
-    for (int k = 0; k < 16; ++k) { const h2 v = q2[h][16 * g + k]; s += (float)v.x + (float)v.y; }
-    qg[h][g] = s;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Stage 1: pseudo-max over support tokens [0, min(S,L)) U [max(0,L-W), L),
 // exact scores with K-hat.  Grid (npart, Hkv, B), 4 waves: work-group `part`
@@ -208,14 +221,14 @@ __device__ inline void group_sums(const h2 (*q2)[64], float (*qg)[kGroups], int 
 template <int G>
 __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   constexpr int NT = QFrags<G>::NT;
-  __shared__ h2 q2[G][64];
-  __shared__ float qg[G][kGroups];
   __shared__ float red[kWaves][G];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
-  stage_q<G>(p, b, qh0, tid, q2);
+  __shared__ uint32_t qs[G * 64];
+  typename QFrags<G>::Stage qst;
+  QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
   const int s_end = min(p.sink, L);
@@ -231,11 +244,12 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   const uint4 zw = *reinterpret_cast<const uint4*>(p.sz + bi * kSzBytes + to.sz);
   uint2 R[kGroups], S8;
   load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, R, S8);
+  QFrags<G>::stage_store(qst, tid, qs);
   __syncthreads();
-  group_sums<G>(q2, qg, tid);
-  __syncthreads();
+  typename QFrags<G>::Load ql;
+  QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
-  qf.build(q2, qg, lane);
+  qf.build(ql, lane);
   float e[NT][4], r[NT][4];
   qf.estimate(cw, zw, e);
   qf.residual(R, S8, r);
@@ -496,25 +510,28 @@ struct MfmaSoftmax {
 
 // ---------------------------------------------------------------------------
 // Stages 2 + 3 for one chunk of blocks.
+//   prologue: first thumbnail batch, the lane's q share and the parts of its
+//            head's pseudo-max are loaded at once; no barrier before the scan
 //   phase A: every wave estimates its tile of every block of the chunk (loads
 //            double-buffered in batches of 4 blocks); estimates stay in LDS
-//   decide:  block kept if it holds a support token, or some head's block
-//            max of the estimate reaches that head's threshold
+//            and the wave records whether some head of the tile reaches its
+//            threshold m~ - delta
+//   decide:  a block is kept if it holds a support token or some wave's tile
+//            reached a threshold; every wave derives the same kept mask
 //   phase B: every wave refines its tile of every kept block (residual, rscale
 //            and V of the next kept block loaded while the current one is
 //            computed), online softmax, P.V on MFMA
-// Dynamic LDS: per-block estimates [cb][4 waves][G][16] (reused by the
-// combine) followed by per-(block, wave, row group) maxima [cb][16][G].
+// Dynamic LDS: per-block estimates [cb][4 waves][G][16], per-(block, wave, row
+// group) maxima [cb][16][G] (written only for the block-max diagnostic), the
+// combine area.
 // ---------------------------------------------------------------------------
 template <int G>
 struct AttendCfg {
   static constexpr int NT = QFrags<G>::NT;
   static constexpr int CBMAX = (G <= 4) ? 32 : 16;
   static constexpr size_t est_bytes(int cb) { return (size_t)cb * kWaves * G * 16 * sizeof(float); }
-  static constexpr size_t lds_bytes(int cb) {
-    return (est_bytes(cb) > sizeof(CombineLds<G>) ? est_bytes(cb) : sizeof(CombineLds<G>)) +
-           (size_t)cb * 4 * kWaves * G * sizeof(float);
-  }
+  static constexpr size_t tmax_bytes(int cb) { return (size_t)cb * 4 * kWaves * G * sizeof(float); }
+  static constexpr size_t lds_bytes(int cb) { return est_bytes(cb) + tmax_bytes(cb) + sizeof(CombineLds<G>); }
 };
 
 struct RefineRegs {
@@ -530,6 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     DecodeParams p) {
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
   const int blk0 = chunk * p.cb;
   const int nbl_cap = min(p.cb, p.nblk_cap - blk0);
@@ -540,7 +558,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const uint8_t* cbase = p.codes + bi0 * kCodesBytes + to.codes;
   const uint8_t* zbase = p.sz + bi0 * kSzBytes + to.sz;
 
-  // first thumbnail batch: independent of the sequence length and of q
+  // ---- prologue: all loads issued together (q first: it is stored to LDS
+  // while the thumbnail batch is still in flight) ----
+  typename QFrags<G>::Stage qst;
+  QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
   uint2 cwA[4], cwB[4];
   uint4 zwA[4], zwB[4];
   auto load_batch = [&](int j0, uint2 (&cw)[4], uint4 (&zw)[4]) {
@@ -552,41 +573,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     }
   };
   load_batch(0, cwA, zwA);
+  // partial pseudo-maxima (part pp, head h) at thread pp*G + h, one load per
+  // thread (maximum over several parts when there are more than 256/G)
+  const int n_pm = p.npart * G;
+  float pm_t = -INFINITY;
+  {
+    const float* pm = p.pmax + (size_t)b * p.npart * p.Hq + qh0;
+    if (tid < n_pm) pm_t = pm[(size_t)(tid / G) * p.Hq + tid % G];
+    for (int i = tid + (256 / G) * G; i < n_pm; i += (256 / G) * G) pm_t = fmaxf(pm_t, pm[(size_t)(i / G) * p.Hq + i % G]);
+  }
 
-  __shared__ h2 q2[G][64];
-  __shared__ float qg[G][kGroups];
-  __shared__ float thr_s[G];
-  __shared__ int klist[CBMAX];
-  __shared__ int nkeep;
+  __shared__ uint32_t qs[G * 64];
+  __shared__ float pm_s[256];
+  QFrags<G>::stage_store(qst, tid, qs);
+  __shared__ int kflag[kWaves][CBMAX];  // wave's tile of block j reached a threshold
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
   float* est = dyn;                                                // [cb][kWaves][G][16]
   float* tmax = dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float);  // [cb][4*kWaves][G]
-  if (AttendCfg<G>::est_bytes(cb) < sizeof(CombineLds<G>)) tmax = dyn + sizeof(CombineLds<G>) / sizeof(float);
-  CombineLds<G>& cl = *reinterpret_cast<CombineLds<G>*>(dyn);
+  CombineLds<G>& cl =
+      *reinterpret_cast<CombineLds<G>*>(dyn + (AttendCfg<G>::est_bytes(cb) + AttendCfg<G>::tmax_bytes(cb)) / sizeof(float));
 
-  stage_q<G>(p, b, qh0, tid, q2);
-  float mt = -INFINITY;  // pseudo-max of head `tid`: max over the parts (loads issued with the others)
-  if (tid < G)
-    for (int pp = 0; pp < p.npart; ++pp) mt = fmaxf(mt, p.pmax[((size_t)b * p.npart + pp) * p.Hq + qh0 + tid]);
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
   if (blk0 >= nblk) return;
   const int nbl = min(p.cb, nblk - blk0);
-  if (tid < G) {
-    thr_s[tid] = mt - p.delta;
-    if (chunk == 0 && p.dbg_mt) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = mt;
-  }
-  __syncthreads();
-  group_sums<G>(q2, qg, tid);
-  __syncthreads();
-  QFrags<G> qf;
-  qf.build(q2, qg, lane);
-  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
-  // Drain every load issued so far (first batch, q, the pseudo-max parts of a
-  // runtime-length loop) so that the pipelined scan below starts from an exact
-  // count of loads in flight.
+  const bool dbg_bmax = p.dbg_bmax != nullptr;
+  // Drain every load issued so far (first batch, q, the pseudo-max parts) so
+  // that the pipelined scan below starts from an exact count of loads in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  pm_s[tid] = pm_t;
+  __syncthreads();
+  typename QFrags<G>::Load ql;
+  QFrags<G>::load(qs, lane, ql);
+  QFrags<G> qf;
+  qf.build(ql, lane);
+  // pseudo-max of head h: maximum over the parts of the per-thread values
+  const int n_pt = min(n_pm, (256 / G) * G) / G;  // parts held in pm_s
+  auto pseudo_max = [&](int h) {
+    float m = -INFINITY;
+    for (int pp = 0; pp < n_pt; ++pp) m = fmaxf(m, pm_s[pp * G + h]);
+    return m;
+  };
+  float thr[NT];  // threshold of the lane column's head, in dot-product units
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int h = 4 * nt + hc;
+    thr[nt] = h < G ? (pseudo_max(h) - p.delta) / p.sm_scale : INFINITY;
+  }
+  if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
@@ -605,16 +640,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
             for (int i = 0; i < 4; ++i) e[nt][i] = (row0 + i < L) ? e[nt][i] : -INFINITY;
         }
+        bool reach = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const float mx = fmaxf(fmaxf(e[nt][0], e[nt][1]), fmaxf(e[nt][2], e[nt][3]));
+          reach = reach || (mx >= thr[nt]);
           const int h = 4 * nt + hc;
           if (gc == 0 && h < G) {
             *reinterpret_cast<float4*>(&est[((j * kWaves + wave) * G + h) * 16 + 4 * ks]) =
                 make_float4(e[nt][0], e[nt][1], e[nt][2], e[nt][3]);
-            tmax[(j * 4 * kWaves + 4 * wave + ks) * G + h] = mx;
+            if (dbg_bmax) tmax[(j * 4 * kWaves + 4 * wave + ks) * G + h] = mx;
           }
         }
+        const bool any = __builtin_amdgcn_ballot_w64(reach) != 0;
+        if (lane == 0) kflag[wave][j] = any ? 1 : 0;
       }
     }
   };
@@ -631,32 +670,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   }
   __syncthreads();
 
-  // ---- block decisions: forced (sink/local) or some head reaches its threshold ----
-  if (wave == 0) {
+  // ---- block decisions (every wave derives the same mask) ----
+  uint64_t kmask;
+  {
     bool kp = false;
     if (lane < nbl) {
       const int blk = blk0 + lane;
       const int sink_end = p.sink > 0 ? ((min(p.sink, L) + 63) >> 6) : 0;
       const int local_beg = p.local > 0 ? (max(0, L - p.local) >> 6) : nblk;
-      kp = blk < sink_end || blk >= local_beg;
+      kp = blk < sink_end || blk >= local_beg || kflag[0][lane] || kflag[1][lane] || kflag[2][lane] ||
+           kflag[3][lane];
+      if (wave == 0) {
+        if (p.dbg_keep) p.dbg_keep[head * p.nblk_cap + blk] = kp ? 1 : 0;
+        if (dbg_bmax) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* tm = tmax + lane * 4 * kWaves * G + h;
-        float bm = tm[0];
+          for (int h = 0; h < G; ++h) {
+            const float* tm = tmax + lane * 4 * kWaves * G + h;
+            float bm = tm[0];
 #pragma unroll
-        for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tm[r * G]);
-        bm *= p.sm_scale;
-        kp = kp || (bm >= thr_s[h]);
-        if (p.dbg_bmax) p.dbg_bmax[((size_t)b * p.Hq + qh0 + h) * p.nblk_cap + blk] = bm;
+            for (int r = 1; r < 4 * kWaves; ++r) bm = fmaxf(bm, tm[r * G]);
+            p.dbg_bmax[((size_t)b * p.Hq + qh0 + h) * p.nblk_cap + blk] = bm * p.sm_scale;
+          }
+        }
       }
-      if (p.dbg_keep) p.dbg_keep[head * p.nblk_cap + blk] = kp ? 1 : 0;
     }
-    const uint64_t mask = __ballot(kp);
-    if (kp) klist[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
-    if (lane == 0) nkeep = __popcll(mask);
+    kmask = __builtin_amdgcn_ballot_w64(kp);
   }
-  __syncthreads();
-  const int K = nkeep;
 
   // ---- phase B: refine tile `wave` of every kept block ----
   MfmaSoftmax<NT> st;
@@ -712,19 +751,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       }
       st.step(xs, c2, slack, va);
     };
-    // next kept block loaded while the current one is computed; as in the
-    // scan, unconditionally (the last block is re-read past the end of the list)
+    // kept blocks in increasing order from the (wave-uniform) mask; the next
+    // one is loaded while the current one is computed, unconditionally as in
+    // the scan (the last block is re-read past the end of the mask)
+    uint64_t rem = kmask;
     RefineRegs X, Y;
-    if (K > 0) load_block(klist[0], X);
-    for (int kk = 0; kk < K; kk += 2) {
-      load_block(klist[min(kk + 1, K - 1)], Y);
-      refine(klist[kk], X);
-      if (kk + 1 >= K) break;
-      load_block(klist[min(kk + 2, K - 1)], X);
-      refine(klist[kk + 1], Y);
+    if (rem) load_block(__builtin_ctzll(rem), X);
+    while (rem) {
+      const int jx = __builtin_ctzll(rem);
+      rem &= rem - 1;
+      const int jy = rem ? __builtin_ctzll(rem) : jx;
+      load_block(jy, Y);
+      refine(jx, X);
+      if (!rem) break;
+      rem &= rem - 1;
+      const int jn = rem ? __builtin_ctzll(rem) : jy;
+      load_block(jn, X);
+      refine(jy, Y);
     }
   }
-  __syncthreads();  // est is no longer read: its LDS is reused by the combine
   st.template store<G>(cl, wave, lane, p.sm_scale);
   __syncthreads();
   combine_chunk<G>(p, cl, tid, b, hkv, chunk);
@@ -758,28 +803,23 @@ __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
     for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
   };
   load_block(0);
-  __shared__ h2 q2[G][64];
+  // B fragments: column col = head, k-slice ks of each group (zero past G)
+  h8 Bd[kGroups];
+  {
+    const uint16_t* qh = p.q + ((size_t)b * p.Hq + qh0 + (col < G ? col : 0)) * kHeadDim + 8 * ks;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      uint4 f = make_uint4(0, 0, 0, 0);
+      if (col < G) f = *reinterpret_cast<const uint4*>(qh + 32 * g);
+      Bd[g] = __builtin_bit_cast(h8, f);
+    }
+  }
   __shared__ float pw[kWaves][16 * PG];
   __shared__ CombineLds<G> cl;
-  stage_q<G>(p, b, qh0, tid, q2);
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
   if (blk0 >= nblk) return;
   const int nbl = min(p.cb, nblk - blk0);
-  __syncthreads();
-  h8 Bd[kGroups];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    h8 f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      h2 pr = {(_Float16)0.f, (_Float16)0.f};
-      if (col < G) pr = q2[col][16 * g + 4 * ks + d];
-      f[2 * d] = pr.x;
-      f[2 * d + 1] = pr.y;
-    }
-    Bd[g] = f;
-  }
   WaveSoftmax<G, 1> st;
   st.init();
   float* pwv = pw[wave];
