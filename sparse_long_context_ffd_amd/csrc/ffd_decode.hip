@@ -555,8 +555,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const int qh0 = hkv * G;
   const TileOffsets to(wave, lane);
   const size_t bi0 = head * p.nblk_cap + blk0;
-  const uint8_t* cbase = p.codes + bi0 * kCodesBytes + to.codes;
-  const uint8_t* zbase = p.sz + bi0 * kSzBytes + to.sz;
+  // per-head buffer descriptors; lane offsets in VGPRs, block offsets in SGPRs
+  const size_t hb = head * p.nblk_cap;  // first block of the head
+  const uint32_t nbc = (uint32_t)p.nblk_cap;
+  const __amdgpu_buffer_rsrc_t r_codes = make_rsrc(p.codes + hb * kCodesBytes, nbc * kCodesBytes);
+  const __amdgpu_buffer_rsrc_t r_sz = make_rsrc(p.sz + hb * kSzBytes, nbc * kSzBytes);
 
   // ---- prologue: all loads issued together (q first: it is stored to LDS
   // while the thumbnail batch is still in flight) ----
@@ -568,8 +571,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int jj = min(j0 + v, nbl_cap - 1);
-      cw[v] = *reinterpret_cast<const uint2*>(cbase + (size_t)jj * kCodesBytes);
-      zw[v] = *reinterpret_cast<const uint4*>(zbase + (size_t)jj * kSzBytes);
+      cw[v] = buf_load_b64(r_codes, (uint32_t)to.codes, (uint32_t)(blk0 + jj) * kCodesBytes);
+      zw[v] = buf_load_b128(r_sz, (uint32_t)to.sz, (uint32_t)(blk0 + jj) * kSzBytes);
     }
   };
   load_batch(0, cwA, zwA);
@@ -657,10 +660,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       }
     }
   };
-  // The next batch is loaded unconditionally (indices clamped to the chunk, so
-  // a batch past the end re-reads the last block from L2): every path then
-  // issues the same number of loads, which lets the compiler's load counters
-  // wait for the batch being scanned only, not for the one in flight.
+  // Two batches alternate: one is in flight while the other is scanned.  The
+  // loads are unconditional (indices clamped to the chunk, so a batch past the
+  // end re-reads the last block from L2): every path then issues the same
+  // number of loads, which lets the compiler's load counters wait for the
+  // batch being scanned only, not for the one in flight.
   for (int j0 = 0; j0 < nbl; j0 += 8) {
     load_batch(j0 + 4, cwB, zwB);
     scan_batch(j0, cwA, zwA);
@@ -702,14 +706,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   st.init();
   {
     // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes)
-    const size_t v_lane = (size_t)((4 * wave + ks) * kHeadDim + 8 * col) * 4;
+    const uint32_t v_lane = (uint32_t)(((4 * wave + ks) * kHeadDim + 8 * col) * 4 * sizeof(uint16_t));
+    const __amdgpu_buffer_rsrc_t r_res = make_rsrc(p.res + hb * kResBytes, nbc * kResBytes);
+    const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
+    const __amdgpu_buffer_rsrc_t r_v = make_rsrc(p.v + head * p.L_cap * kHeadDim, nbc * kVBytes);
     auto load_block = [&](int j, RefineRegs& x) {
-      const size_t bi = bi0 + j;
-      load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, x.R, x.S8);
-      const uint4* vb = reinterpret_cast<const uint4*>(p.v + (head * p.L_cap + (size_t)(blk0 + j) * 64) * kHeadDim +
-                                                       v_lane);
+      const uint32_t blk = (uint32_t)(blk0 + j);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x.V[q] = vb[q];
+      for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
+      x.S8 = buf_load_b64(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
     };
     const float c2 = p.sm_scale * kLog2e, slack = 8.f / c2;
     auto refine = [&](int j, RefineRegs& x) {

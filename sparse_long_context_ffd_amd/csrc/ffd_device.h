@@ -89,6 +89,23 @@ __device__ inline float rows_sum(float v) {
   return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
 }
 
+// Buffer loads: a wave-uniform descriptor (base, size in bytes) plus a 32-bit
+// lane offset (VGPR) and a wave-uniform offset (SGPR).  Streaming loads in this
+// form need no per-load 64-bit address registers, so the compiler never has to
+// wait for a load in flight just to reuse an address register.  Offsets at or
+// past `bytes` read as zero.  (Descriptor word 3 value for gfx9 raw buffers.)
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline uint2 buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ inline uint4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // A 32-bit constant in a VGPR whose value the compiler cannot see.  With the
 // mask in an SGPR and the constant in a VGPR, (x & mask) | bits is selected as
 // one v_and_or_b32 (with both as visible literals the compiler emits two
