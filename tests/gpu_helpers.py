@@ -68,12 +68,13 @@ def cache_to_host(cache):
     return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
-def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE):
+def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None):
     import sparse_long_context_ffd_amd as ffd
     B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
     nb = shape.max_seq_len // 64
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
-    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     dbg = {
         "m_tilde": torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda"),
         "bmax": torch.full((B, Hq, nb), float("nan"), dtype=torch.float32, device="cuda"),

@@ -159,3 +159,27 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out_g, ref), f"replay {r} differs from the eager result"
         assert torch.isfinite(junk)
+
+
+def test_workspace_reuse_across_calls():
+    """Calls in a row on one workspace with different queries each match the
+    oracle, and a repeated query gives the same bits: nothing a call leaves in
+    the workspace leaks into the next one."""
+    torch = torch_mod()
+    w = WORKLOADS["tiny_h4x1_4k"]
+    c = make_case(w, 2)
+    shape = shape_for(w)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
+    import sparse_long_context_ffd_amd as ffd
+    ws = torch.full((ffd.workspace_bytes(shape),), 0x7F, dtype=torch.uint8, device="cuda")
+    lens = dev(c["seq_lens"], torch)
+    q2 = (np.random.default_rng(9).standard_normal(c["q"].shape) * 1.5).astype(np.float16)
+    pk = orc.quantize_k(c["k"][0, 0])
+    outs = []
+    for r, q in enumerate((c["q"], q2, c["q"], q2, q2)):
+        say(f"workspace reuse call {r}")
+        got = gpu_decode(shape, dev(q, torch), cache, lens, 5.0, torch, ws=ws)
+        check_head(orc, q[0], pk, c["v"][0, 0], 4096, 5.0, got, 0, 0, w.group, label=f"reuse call {r}")
+        outs.append(got["out"])
+    assert np.array_equal(outs[0], outs[2])
+    assert np.array_equal(outs[1], outs[3]) and np.array_equal(outs[1], outs[4])
