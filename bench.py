@@ -169,6 +169,19 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     g_warm, g_steps, g_attend = graph_of([lambda i=i: step(i) for i in range(warmup)], torch), \
         graph_of([lambda i=i: step(i) for i in range(steps)], torch), \
         graph_of([lambda i=i: step(i, stages=2) for i in range(steps)], torch)
+    # decode loop: each step first appends one token per sequence (its last one,
+    # rewritten with the same key and value, so the cache and the work stay fixed)
+    last = d["seq_lens"].long() - 1
+    bidx = torch.arange(w.batch, device="cuda")
+    k_last = d["k"][bidx, :, last].contiguous()          # [B][Hkv][128]
+    v_last = d["v"][bidx, :, last].contiguous()
+    pos = (d["seq_lens"] - 1).to(torch.int32).contiguous()
+
+    def loop_step(i):
+        ffd.append_kv(shape, k_last, v_last, pos, layers[i % R])
+        step(i)
+
+    g_loop = graph_of([lambda i=i: loop_step(i) for i in range(steps)], torch)
     g_warm.replay()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -176,6 +189,8 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     wall = time.perf_counter() - wall0
     g_attend.replay()
     attend_total_ms = timed_replay(g_attend, torch)
+    g_loop.replay()
+    loop_total_ms = timed_replay(g_loop, torch)
     us_step = total_ms * 1e3 / steps
     attend_us = attend_total_ms * 1e3 / steps
     return {
@@ -183,6 +198,7 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
         "wall_us_per_step": wall * 1e6 / steps,
         "eager_us_per_step": eager_us,
         "attend_us_mean": attend_us,
+        "loop_us_per_step": loop_total_ms * 1e3 / steps,
         "keep_fraction": keep_frac,
         "attend_bytes": attend_bytes,
         "step_bytes": step_bytes,
@@ -303,6 +319,7 @@ def main():
         "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
         "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
         "attend_kernel_us": round(r["attend_us_mean"], 3),
+        "decode_loop_us_per_step": round(r["loop_us_per_step"], 3),
         "dense_us_per_step": round(dense["us_per_step"], 3),
         "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -322,6 +339,7 @@ def main():
         result["long_context"] = {
             "workload": wl.name, "delta": wl.deltas[0], "us_per_step": round(rl["us_per_step"], 3),
             "keep_fraction": round(rl["keep_fraction"], 5), "attend_kernel_us": round(rl["attend_us_mean"], 3),
+            "decode_loop_us_per_step": round(rl["loop_us_per_step"], 3),
             "effective_gbps": round(rl["step_bytes"] / (rl["us_per_step"] * 1e3), 1),
             "roofline_attend": {"achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
                                 "traffic": traffic_bytes(wl.name), "bytes_per_launch": rl["attend_bytes"]},

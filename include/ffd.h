@@ -159,6 +159,20 @@ int ffd_quantize_k(const ffd_shape_t* shape, const void* k, int32_t t_begin, int
 int ffd_pack_v(const ffd_shape_t* shape, const void* v, int32_t t_begin, int32_t t_end,
                const ffd_cache_t* cache, void* stream);
 
+/* Decode-loop append (the decode step writes the new token's key and value
+ * before attending; the page's Method section captures the step in graphs to
+ * remove launch overhead): quantize one new key per (b, kv head) exactly as
+ * ffd_quantize_k does and store its value as ffd_pack_v does, at token index
+ * pos[b], a position read on the device so that the call can be captured in a
+ * graph with ffd_decode_attn.
+ *   k_new, v_new  fp16 [B][Hkv][128], natural order, 16-byte aligned
+ *   pos           int32 [B] device array; a position outside
+ *                 [0, max_seq_len) skips that sequence (nothing is written)
+ *   cache         every field is written at the token; other tokens untouched
+ * The usual loop appends at pos = L then decodes with seq_lens = L + 1. */
+int ffd_append_kv(const ffd_shape_t* shape, const void* k_new, const void* v_new, const int32_t* pos,
+                  const ffd_cache_t* cache, void* stream);
+
 /* One FFD decode-attention step (Method 3 stages 1-3 plus the log-sum-exp
  * merge of per-chunk partials).
  *   q         fp16 [B][Hq][128]

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PackedCache,
     Shape,
+    append_kv,
     cache_bytes,
     decode_attn,
     dense_decode_attn,
@@ -22,6 +23,6 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "cache_bytes", "decode_attn",
+    "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn",
     "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "quantize_k", "strerror", "workspace_bytes",
 ]

@@ -20,7 +20,8 @@ STATUS = {
     -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP",
 }
 EXPORTED = (
-    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_decode_attn",
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
+    "ffd_decode_attn",
     "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
 )
 
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
         L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_pack_v.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
+        L.ffd_append_kv.argtypes = [P(Shape), V, V, V, P(Cache), V]
         L.ffd_decode_attn.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, V, V, SZ,
                                       P(Debug), V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
@@ -171,6 +173,21 @@ def pack_v(shape: Shape, v, t_begin: int, t_end: int, cache: PackedCache, stream
     c = cache.c_struct()
     _check(lib().ffd_pack_v(ctypes.byref(shape), _ptr(v), int(t_begin), int(t_end), ctypes.byref(c),
                             _stream(stream)), "ffd_pack_v")
+
+
+def append_kv(shape: Shape, k_new, v_new, pos, cache: PackedCache, stream=None) -> None:
+    """Write one token per sequence at the device positions ``pos`` (int32 [B])."""
+    import torch
+    n = shape.batch * shape.num_kv_heads * 128
+    _need(k_new, torch.float16, n, "k_new")
+    _need(v_new, torch.float16, n, "v_new")
+    _need(pos, torch.int32, shape.batch, "pos")
+    nb = cache_bytes(shape)
+    for f in FIELDS:
+        _need(getattr(cache, f), torch.uint8, nb[f], f"cache.{f}")
+    c = cache.c_struct()
+    _check(lib().ffd_append_kv(ctypes.byref(shape), _ptr(k_new), _ptr(v_new), _ptr(pos), ctypes.byref(c),
+                               _stream(stream)), "ffd_append_kv")
 
 
 def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,

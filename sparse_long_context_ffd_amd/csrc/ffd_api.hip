@@ -84,7 +84,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 extern "C" {
 
-int ffd_version(void) { return 200; }
+int ffd_version(void) { return 300; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -157,6 +157,22 @@ int ffd_pack_v(const ffd_shape_t* shape, const void* v, int32_t t_begin, int32_t
   if (t_end == t_begin) return FFD_OK;
   return from_hip(ffd::launch_pack_v(v, shape->batch, shape->num_kv_heads, shape->max_seq_len, t_begin, t_end,
                                      cache->v, static_cast<hipStream_t>(stream)));
+}
+
+int ffd_append_kv(const ffd_shape_t* shape, const void* k_new, const void* v_new, const int32_t* pos,
+                  const ffd_cache_t* cache, void* stream) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!k_new || !v_new || !pos || !cache || !cache->codes || !cache->sz || !cache->res || !cache->rscale ||
+      !cache->v)
+    return FFD_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cache->codes) || !aligned16(cache->sz) ||
+      !aligned16(cache->res) || !aligned16(cache->rscale) || !aligned16(cache->v) ||
+      (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return FFD_ERR_ALIGN;
+  return from_hip(ffd::launch_append(k_new, v_new, pos, shape->batch, shape->num_kv_heads, shape->max_seq_len,
+                                     cache->codes, cache->sz, cache->res, cache->rscale, cache->v,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,

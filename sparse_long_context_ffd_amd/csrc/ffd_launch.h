@@ -33,6 +33,8 @@ hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, in
                        void* sz, void* res, void* rsc, hipStream_t stream);
 hipError_t launch_pack_v(const void* v, int B, int Hkv, int L_cap, int t_begin, int t_end, void* vt,
                          hipStream_t stream);
+hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* pos, int B, int Hkv, int L_cap,
+                         void* codes, void* sz, void* res, void* rsc, void* vt, hipStream_t stream);
 hipError_t launch_ffd_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_dense_decode(const DecodeParams& p, hipStream_t s);
 

@@ -13,7 +13,8 @@
 // double rounding to differ from rounding the exact quotient).
 //
 // Launch: grid (ceil(n/64), Hkv, B), 256 threads; thread = (token, group),
-// 4 threads per token, 64 tokens per work-group.
+// 4 threads per token, 64 tokens per work-group.  The decode-loop append runs
+// the same per-group quantizer for one token per (sequence, KV head).
 #include "ffd_device.h"
 #include "ffd_launch.h"
 
@@ -46,26 +47,20 @@ __device__ inline double f16bits_to_f64(uint16_t b) {
   return (double)__builtin_bit_cast(_Float16, b);
 }
 
-__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ k, int L_cap,
-                                                   int t_begin, int t_end,
-                                                   uint32_t* __restrict__ codes,
-                                                   uint32_t* __restrict__ sz,
-                                                   int8_t* __restrict__ res,
-                                                   uint16_t* __restrict__ rsc) {
-  const int tid = threadIdx.x;
-  const int g = tid & 3;
-  const int t = t_begin + blockIdx.x * 64 + (tid >> 2);
-  const bool active = t < t_end;
-  const size_t head = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
-  const int nblk_cap = L_cap >> 6;
-  const int tc = active ? t : t_begin;  // inactive threads read a valid row and store nothing
-
-  // 32 fp16 values of this (token, group)
-  const uint4* src = reinterpret_cast<const uint4*>(k + (head * L_cap + tc) * kHeadDim + g * kGroup);
+// Quantize one (token, group) -- 32 fp16 keys at `src` -- and store its code
+// bits, (scale, zero), residual bytes and residual scale at token t of head
+// `head`.  The code word of a token is shared by the groups g and g ^ 1, which
+// must sit in the lanes lane and lane ^ 1 of the same wave (both lanes active,
+// same token); `store` = false computes and takes part in that exchange but
+// writes nothing.
+__device__ inline void pack_group(const uint16_t* __restrict__ src, size_t head, int nblk_cap, int t, int g,
+                                  bool store, uint32_t* __restrict__ codes, uint32_t* __restrict__ sz,
+                                  int8_t* __restrict__ res, uint16_t* __restrict__ rsc) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
   uint32_t w[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 v = src[i];
+    const uint4 v = s4[i];
     w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
   double x[32];
@@ -127,7 +122,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq) other[kq] = (uint32_t)__shfl_xor((int)frag[kq], 1, 64);
 
-  if (!active) return;
+  if (!store) return;
   const int blk = t >> 6, tb = t & 63;
   const size_t blk_idx = head * nblk_cap + blk;
   uint8_t* cbase = reinterpret_cast<uint8_t*>(codes) + blk_idx * kCodesBytes;
@@ -146,6 +141,48 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   *reinterpret_cast<uint4*>(rbase + res_off(tb, 32 * g + 16)) = make_uint4(rw[4], rw[5], rw[6], rw[7]);
   uint8_t* sbase = reinterpret_cast<uint8_t*>(rsc) + blk_idx * kRscBytes;
   *reinterpret_cast<uint16_t*>(sbase + rsc_off(tb, g)) = s8b;
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ k, int L_cap,
+                                                   int t_begin, int t_end,
+                                                   uint32_t* __restrict__ codes,
+                                                   uint32_t* __restrict__ sz,
+                                                   int8_t* __restrict__ res,
+                                                   uint16_t* __restrict__ rsc) {
+  const int tid = threadIdx.x;
+  const int g = tid & 3;
+  const int t = t_begin + blockIdx.x * 64 + (tid >> 2);
+  const bool active = t < t_end;
+  const size_t head = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int tc = active ? t : t_begin;  // inactive threads read a valid row and store nothing
+  pack_group(k + (head * L_cap + tc) * kHeadDim + g * kGroup, head, L_cap >> 6, tc, g, active, codes, sz, res,
+             rsc);
+}
+
+// Decode-loop append: one new token per (sequence, KV head), written at the
+// sequence's own position pos[b] read on the device (so the append can sit in a
+// captured graph beside the decode step).  One wave per (b, kv head): lanes
+// 0..3 quantize the four groups of the key (every lane computes group lane & 3
+// so that the code-word exchange has both partners; lanes >= 4 store nothing);
+// lane = channel pair for the value, stored into the token-quad tiled layout.
+// A position outside [0, L_cap) skips the sequence.
+__global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__ k_new,
+                                                    const uint16_t* __restrict__ v_new,
+                                                    const int32_t* __restrict__ pos, int L_cap,
+                                                    uint32_t* __restrict__ codes, uint32_t* __restrict__ sz,
+                                                    int8_t* __restrict__ res, uint16_t* __restrict__ rsc,
+                                                    uint16_t* __restrict__ vt) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.y;
+  const size_t head = (size_t)b * gridDim.x + blockIdx.x;
+  const int t = pos[b];
+  if (t < 0 || t >= L_cap) return;  // uniform over the work-group
+  const int g = lane & 3;
+  pack_group(k_new + head * kHeadDim + g * kGroup, head, L_cap >> 6, t, g, lane < 4, codes, sz, res, rsc);
+  const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_new + head * kHeadDim + 2 * lane);
+  uint16_t* dst = vt + (head * L_cap + (size_t)(t & ~3)) * kHeadDim + 8 * lane + (t & 3);
+  dst[0] = (uint16_t)(vv & 0xffffu);  // channel 2*lane
+  dst[4] = (uint16_t)(vv >> 16);      // channel 2*lane + 1
 }
 
 // V pack: natural fp16 rows -> the token-quad tiled layout the refine's
@@ -205,6 +242,15 @@ hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, in
   hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(k), L_cap,
                      t_begin, t_end, static_cast<uint32_t*>(codes), static_cast<uint32_t*>(sz),
                      static_cast<int8_t*>(res), static_cast<uint16_t*>(rsc));
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* pos, int B, int Hkv, int L_cap,
+                         void* codes, void* sz, void* res, void* rsc, void* vt, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(Hkv, B), dim3(64), 0, stream, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), pos, L_cap, static_cast<uint32_t*>(codes),
+                     static_cast<uint32_t*>(sz), static_cast<int8_t*>(res), static_cast<uint16_t*>(rsc),
+                     static_cast<uint16_t*>(vt));
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 200
+    assert L.ffd_version() == 300
 
 
 def test_strerror_covers_codes():
@@ -121,6 +121,18 @@ def test_dense_and_pack_argument_errors():
     assert L.ffd_pack_v(ctypes.byref(s), FAKE + 2, 0, 5, ctypes.byref(cv), None) == -3
     assert L.ffd_pack_v(ctypes.byref(s), FAKE, 0, 5, ctypes.byref(_lib.Cache(None, None, None, None, FAKE + 8)),
                         None) == -3
+    full = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.ffd_append_kv(ctypes.byref(s), None, FAKE, FAKE, ctypes.byref(full), None) == -1
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, None, FAKE, ctypes.byref(full), None) == -1
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(full), None) == -1
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(c), None) == -1     # cache->v NULL
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE + 2, FAKE, FAKE, ctypes.byref(full), None) == -3
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, FAKE + 8, FAKE, ctypes.byref(full), None) == -3
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, FAKE, FAKE + 2, ctypes.byref(full), None) == -3
+    assert L.ffd_append_kv(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(_lib.Cache(FAKE, FAKE, FAKE + 4, FAKE,
+                                                                                      FAKE)), None) == -3
+    bad = _lib.Shape(1, 4, 1, 64, 64, 64, 256, 4096, 0)
+    assert L.ffd_append_kv(ctypes.byref(bad), FAKE, FAKE, FAKE, ctypes.byref(full), None) == -2
 
 
 def test_cache_and_workspace_sizes():

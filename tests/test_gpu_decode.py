@@ -10,7 +10,7 @@ import pytest
 
 from oracle import ffd_oracle as orc
 from synthetic import WORKLOADS, Workload, make_case
-from tests.gpu_helpers import (SM_SCALE, check_head, dev, gpu_decode, gpu_dense, gpu_pack, say,
+from tests.gpu_helpers import (SM_SCALE, cache_to_host, check_head, dev, gpu_decode, gpu_dense, gpu_pack, say,
                                shape_for, torch_mod)
 
 pytestmark = pytest.mark.gpu
@@ -183,3 +183,73 @@ def test_workspace_reuse_across_calls():
         outs.append(got["out"])
     assert np.array_equal(outs[0], outs[2])
     assert np.array_equal(outs[1], outs[3]) and np.array_equal(outs[1], outs[4])
+
+
+def test_decode_loop_append_and_decode_in_one_graph():
+    """Decode loop: one captured graph appends the step's key and value at each
+    sequence's position L (ffd_append_kv), advances the device lengths, and runs
+    the decode step; replayed step after step with new tokens and queries.  At
+    every step the appended cache bytes equal the oracle's quantization and the
+    output matches the oracle over the grown sequences (ragged batch, appends
+    crossing a 64-token block and 4-token quads)."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    from tests.layout import decode_cache
+    w = Workload("loop_b2_h8x2_2k", 2, 8, 2, 2048, None, len_range=(1000, 1500), needles=4)
+    c = make_case(w, 3)
+    B, Hq, Hkv, G, L_cap = w.batch, w.q_heads, w.kv_heads, w.group, w.max_len
+    L0 = np.array([1021, 1497], np.int32)
+    K, V = c["k"].copy(), c["v"].copy()
+    shape = shape_for(w)
+    cache = gpu_pack(shape, dev(K, torch), dev(V, torch))
+    pos = dev(L0, torch)
+    k_new = torch.zeros((B, Hkv, 128), dtype=torch.float16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+    q = torch.zeros((B, Hq, 128), dtype=torch.float16, device="cuda")
+    out = torch.zeros((B, Hq, 128), dtype=torch.float16, device="cuda")
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    nb = L_cap // 64
+    dbg = {"m_tilde": torch.zeros((B, Hq), dtype=torch.float32, device="cuda"),
+           "bmax": torch.zeros((B, Hq, nb), dtype=torch.float32, device="cuda"),
+           "keep": torch.zeros((B, Hkv, nb), dtype=torch.uint8, device="cuda")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ffd.append_kv(shape, k_new, v_new, pos, cache)
+        pos.add_(1)
+        ffd.decode_attn(shape, q, cache, pos, 5.0, SM_SCALE, out, ws, debug=dbg)
+    torch.cuda.synchronize()
+    assert np.array_equal(pos.cpu().numpy(), L0), "capture must not execute the graph"
+    rng = np.random.default_rng(17)
+    for i in range(6):
+        kn = rng.standard_normal((B, Hkv, 128)).astype(np.float16)
+        vn = rng.standard_normal((B, Hkv, 128)).astype(np.float16)
+        qn = rng.standard_normal((B, Hq, 128)).astype(np.float16)
+        k_new.copy_(torch.from_numpy(kn))
+        v_new.copy_(torch.from_numpy(vn))
+        q.copy_(torch.from_numpy(qn))
+        out.fill_(float("nan"))
+        dbg["keep"].fill_(7)
+        torch.cuda.synchronize()
+        say(f"decode loop step {i}")
+        g.replay()
+        torch.cuda.synchronize()
+        L = L0 + i + 1
+        assert np.array_equal(pos.cpu().numpy(), L)
+        for b in range(B):
+            K[b, :, L[b] - 1] = kn[b]
+            V[b, :, L[b] - 1] = vn[b]
+        got = {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
+        raw = decode_cache(**cache_to_host(cache), B=B, Hkv=Hkv, L_cap=L_cap)
+        for b in range(B):
+            for h in range(Hkv):
+                t = L[b] - 1
+                ref = orc.quantize_k(kn[b, h][None])
+                for f in ("codes", "scale", "zero", "res", "rscale"):
+                    a, r = raw[f][b, h, t], ref[f][0]
+                    if a.dtype == np.float16:
+                        a, r = a.view(np.uint16), r.view(np.uint16)
+                    assert np.array_equal(a, r), f"step {i} b{b} h{h}: appended {f} differs"
+                assert np.array_equal(raw["v"][b, h, t].view(np.uint16), vn[b, h].view(np.uint16))
+                pk = orc.quantize_k(K[b, h])
+                check_head(orc, qn[b, h * G:(h + 1) * G], pk, V[b, h], int(L[b]), 5.0, got, b, h, G,
+                           label=f"loop step {i} b{b} h{h}")

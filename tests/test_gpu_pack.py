@@ -142,3 +142,72 @@ def test_pack_v_token_range_leaves_other_bytes_untouched():
         sel[t0:t1] = True
         assert (got[:, :, sel] == v.view(np.uint16)[:, :, sel]).all(), f"range [{t0},{t1})"
         assert (got[:, :, ~sel] == 0xABAB).all(), f"range [{t0},{t1}) touched other tokens"
+
+
+def test_append_kv_matches_oracle_and_skips_out_of_range():
+    """ffd_append_kv writes, for each sequence, exactly the token at its device
+    position: key bytes equal the oracle's quantization of the new key, the
+    value lands unchanged in the tiled layout, positions outside [0, L_cap)
+    write nothing, and every other byte keeps its fill."""
+    torch = torch_mod()
+    rng = np.random.default_rng(21)
+    B, Hkv, L_cap = 6, 2, 256
+    k = rng.standard_normal((B, Hkv, 128))
+    k[1, 0, [3, 50, 97]] *= 5
+    edges = _edge_keys(rng)
+    k[2, 1] = edges[6]                       # on-grid values: zero residual
+    k[3, 0] = edges[1]                       # constant group values
+    k[5, 1] = edges[12]                      # full fp16 range
+    k = k.astype(np.float16)
+    v = rng.standard_normal((B, Hkv, 128)).astype(np.float16)
+    pos = np.array([0, 65, 130, 255, -1, 256], np.int32)   # quad offsets 0..3, then two skips
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(B, 2 * Hkv, Hkv, L_cap)
+    say("append_kv ragged positions")
+    cache = ffd.PackedCache(shape).fill_(0xAB)
+    ffd.append_kv(shape, dev(k, torch), dev(v, torch), dev(pos, torch), cache)
+    torch.cuda.synchronize()
+    got = decode_cache(**cache_to_host(cache), B=B, Hkv=Hkv, L_cap=L_cap)
+    unt = decode_cache(**cache_to_host(ffd.PackedCache(shape).fill_(0xAB)), B=B, Hkv=Hkv, L_cap=L_cap)
+    for b in range(B):
+        for h in range(Hkv):
+            sel = np.zeros(L_cap, bool)
+            if 0 <= pos[b] < L_cap:
+                sel[pos[b]] = True
+                ref = orc.quantize_k(k[b, h][None])
+                ref = {f: ref[f][0] for f in FIELDS}
+                ref["v"] = v[b, h]
+                _assert_fields_equal({f: got[f][b, h, pos[b]][None] for f in FIELDS},
+                                     {f: ref[f][None] for f in FIELDS}, f"append b{b} h{h}")
+                assert np.array_equal(got["v"][b, h, pos[b]].view(np.uint16), v[b, h].view(np.uint16)), \
+                    f"append value b{b} h{h}"
+            for f in FIELDS + ("v",):
+                a, u = got[f][b, h], unt[f][b, h]
+                if a.dtype == np.float16:
+                    a, u = a.view(np.uint16), u.view(np.uint16)
+                assert (a[~sel] == u[~sel]).all(), f"append b{b} h{h} touched other tokens in {f}"
+
+
+def test_append_kv_equals_range_pack():
+    """Appending tokens one call at a time gives the same cache bytes as one
+    ffd_quantize_k + ffd_pack_v over the whole range."""
+    torch = torch_mod()
+    rng = np.random.default_rng(22)
+    B, Hkv, L_cap = 2, 3, 128
+    k = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(B, Hkv, Hkv, L_cap)
+    full = cache_to_host(gpu_pack(shape, dev(k, torch), dev(v, torch), fill=0x5C, t_begin=10, t_end=80))
+    cache = ffd.PackedCache(shape).fill_(0x5C)
+    pos = torch.tensor([10, 10], dtype=torch.int32, device="cuda")
+    say("append_kv 70 steps vs range pack")
+    for t in range(10, 80):
+        kn = dev(np.ascontiguousarray(k[:, :, t]), torch)
+        vn = dev(np.ascontiguousarray(v[:, :, t]), torch)
+        ffd.append_kv(shape, kn, vn, pos, cache)
+        pos += 1
+    torch.cuda.synchronize()
+    got = cache_to_host(cache)
+    for f in ("codes", "sz", "res", "rscale", "v"):
+        assert np.array_equal(got[f], full[f]), f"append loop differs from range pack in {f}"
