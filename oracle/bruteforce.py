@@ -91,8 +91,12 @@ def dot_exact(q: Sequence[float], k: Sequence[Fraction]) -> Fraction:
 
 def decode_head(q: Sequence[Sequence[float]], K: Sequence[Sequence[float]],
                 V: Sequence[Sequence[float]], L: int, delta: float, sm_scale: float,
-                sink: int = 64, local: int = 256) -> Dict[str, object]:
-    """Tiny-input FFD decode for the query heads q (lists of floats) of one KV head."""
+                sink: int = 64, local: int = 256, select: str = "union") -> Dict[str, object]:
+    """Tiny-input FFD decode for the query heads q (lists of floats) of one KV head.
+
+    select: "union" (every token of the kept blocks), "head_block" (kept blocks
+    that are forced or reach the head's own threshold) or "head_token" (support
+    tokens and tokens whose estimate reaches the head's threshold)."""
     toks = [pack_token(K[t]) for t in range(L)]
     G = len(q)
     scale = Fraction(sm_scale)
@@ -110,12 +114,22 @@ def decode_head(q: Sequence[Sequence[float]], K: Sequence[Sequence[float]],
         forced.append(f)
         bmax.append(bm)
         keep.append(f or any(bm[h] >= thr[h] for h in range(G)))
-    out = []
+    out, attended = [], []
     for h in range(G):
-        ts = [t for t in range(L) if keep[t // 64]]
+        ts = []
+        for t in range(L):
+            b = t // 64
+            if not keep[b]:
+                continue
+            if select == "head_block" and not (forced[b] or bmax[b][h] >= thr[h]):
+                continue
+            if select == "head_token" and not (t < sink or t >= L - local or est[h][t] >= thr[h]):
+                continue
+            ts.append(t)
+        attended.append(ts)
         M = max(exact[h][t] for t in ts)
         w = [math.exp(exact[h][t] - M) for t in ts]
         den = math.fsum(w)
         out.append([math.fsum(wi * float(V[t][c]) for wi, t in zip(w, ts)) / den for c in range(len(V[0]))])
     return {"toks": toks, "est": est, "exact": exact, "m_tilde": m_tilde, "thr": thr,
-            "bmax": bmax, "forced": forced, "keep": keep, "out": out}
+            "bmax": bmax, "forced": forced, "keep": keep, "attended": attended, "out": out}

@@ -200,17 +200,37 @@ def lse_merge(parts: Sequence[Tuple[np.ndarray, np.ndarray, np.ndarray]]) -> np.
 # --------------------------------------------------------------------------
 # one decode step for one (sequence, KV head): M3 stages 1-3
 # --------------------------------------------------------------------------
+SELECTIONS = ("union", "head_block", "head_token")
+
+
 def decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: int,
                 delta: float, sm_scale: float, sink: int = 64, local: int = 256,
-                keep: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                keep: Optional[np.ndarray] = None, select: str = "union",
+                tmask: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """FFD decode attention for the G query heads of one KV head.
 
     ``pk`` is the packed cache of that KV head (token axis first, at least L
-    tokens), ``V16`` fp16 [>=L][128].  ``keep`` overrides the selection
-    (used to compare outputs under another implementation's mask).
+    tokens), ``V16`` fp16 [>=L][128].  ``keep`` overrides the block selection
+    and ``tmask`` ([G][L] bool) the tokens each head attends (both used to
+    compare outputs under another implementation's decisions).
+
+    ``select`` chooses what each query head attends inside the blocks kept for
+    the KV head (the loads stay the kept blocks in every case):
+
+    * "union" -- every valid token of every kept block (the block filter of
+      M3 stage 2 shared by the GQA group);
+    * "head_block" -- the kept blocks that are forced or whose largest
+      estimated score reaches this head's own threshold;
+    * "head_token" -- M2's criterion per token and head: the sink and local
+      tokens plus every token whose estimated score reaches this head's
+      threshold.  (The estimate decides, as it does for blocks: exact scores
+      exist only for loaded blocks.)
+
     Returns m_tilde [G], thr [G], s_est [G][L], s_exact [G][L], bmax [G][nblk],
-    forced [nblk], keep [nblk], out [G][128] (fp64).
+    forced [nblk], keep [nblk], tmask [G][L], out [G][128] (fp64).
     """
+    if select not in SELECTIONS:
+        raise ValueError(f"unknown selection {select!r}")
     if L < 1:
         raise ValueError("sequence length must be >= 1")
     deq2, khat = dequantize(slice_tokens(pk, 0, L))
@@ -230,11 +250,26 @@ def decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: 
         keep = sel
     keep = np.asarray(keep, dtype=bool)
 
-    # stage 3: exact attention over every valid token of the kept blocks
+    # which tokens each head attends, inside the kept blocks
+    G = q16.shape[0]
     tok = np.repeat(keep, BLOCK)[:L]
-    out = attend_tokens(s_exact, V16[:L], np.nonzero(tok)[0])
+    if tmask is None:
+        if select == "union":
+            per_head = np.ones((G, L), dtype=bool)
+        elif select == "head_block":
+            hb = forced[None, :] | (bmax >= thr[:, None])
+            per_head = np.repeat(hb, BLOCK, axis=1)[:, :L]
+        else:
+            per_head = sup[None, :] | (s_est >= thr[:, None])
+        tmask = per_head & tok[None, :]
+    tmask = np.asarray(tmask, dtype=bool)
+    if tmask.shape != (G, L):
+        raise ValueError("tmask must be [G][L]")
+
+    # stage 3: exact attention over each head's attended tokens
+    out = np.stack([attend_tokens(s_exact[h:h + 1], V16[:L], np.nonzero(tmask[h])[0])[0] for h in range(G)])
     return {"m_tilde": m_tilde, "thr": thr, "s_est": s_est, "s_exact": s_exact,
-            "bmax": bmax, "forced": forced, "keep": keep, "selected": sel, "out": out}
+            "bmax": bmax, "forced": forced, "keep": keep, "selected": sel, "tmask": tmask, "out": out}
 
 
 def dense_head(q16: np.ndarray, keys: np.ndarray, V16: np.ndarray, L: int,
@@ -255,7 +290,8 @@ def quantize_cache(k: np.ndarray) -> Dict[str, np.ndarray]:
 def decode(q: np.ndarray, pk: Dict[str, np.ndarray], v: np.ndarray, seq_lens: Sequence[int],
            delta: float, sm_scale: float, sink: int = 64, local: int = 256,
            heads: Optional[Iterable[Tuple[int, int]]] = None,
-           keep: Optional[np.ndarray] = None) -> Dict[Tuple[int, int], Dict[str, np.ndarray]]:
+           keep: Optional[np.ndarray] = None,
+           select: str = "union") -> Dict[Tuple[int, int], Dict[str, np.ndarray]]:
     """decode_head for every (b, kv_head) (or the listed ones).
 
     q fp16 [B][Hq][128]; pk fields [B][Hkv][L_cap][...]; v fp16 [B][Hkv][L_cap][128].
@@ -272,7 +308,7 @@ def decode(q: np.ndarray, pk: Dict[str, np.ndarray], v: np.ndarray, seq_lens: Se
         pkh = {f: a[b, h] for f, a in pk.items()}
         kp = None if keep is None else np.asarray(keep[b, h][: n_blocks(L)], dtype=bool)
         res[(b, h)] = decode_head(q[b, h * G:(h + 1) * G], pkh, v[b, h], L, delta, sm_scale,
-                                  sink, local, keep=kp)
+                                  sink, local, keep=kp, select=select)
     return res
 
 

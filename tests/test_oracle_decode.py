@@ -162,3 +162,69 @@ def test_batch_wrapper_gqa_mapping():
             Lb = [L, 100][b]
             one = orc.decode_head(q[b, h * G:(h + 1) * G], orc.quantize_k(k[b, h]), v[b, h], Lb, 5.0, SCALE)
             np.testing.assert_array_equal(res[(b, h)]["out"], one["out"])
+
+
+# ---- selection variants: per-head block sets and per-token masking ----
+
+@pytest.mark.parametrize("select", ["head_block", "head_token"])
+@pytest.mark.parametrize("L,G,sink,local,delta", [
+    (130, 4, 8, 16, 1.0), (400, 4, 8, 16, 1.0), (400, 2, 16, 32, 0.5), (321, 7, 64, 256, 3.0),
+])
+def test_selection_variants_match_bruteforce(select, L, G, sink, local, delta):
+    q, K, V = _case(L, G, seed=L * 7 + G, needles=6)
+    ref = bf.decode_head([list(map(float, r)) for r in q], [list(map(float, r)) for r in K],
+                         V.astype(np.float64).tolist(), L, delta, SCALE, sink, local, select=select)
+    got = orc.decode_head(q, orc.quantize_k(K), V, L, delta, SCALE, sink, local, select=select)
+    for h in range(G):
+        assert list(np.nonzero(got["tmask"][h])[0]) == ref["attended"][h], f"head {h} token set"
+    np.testing.assert_allclose(got["out"], np.array(ref["out"]), rtol=0, atol=1e-12)
+
+
+def test_selection_variants_nest_and_union_is_the_block_filter():
+    """head_token <= head_block <= union per head; the OR of the heads' block
+    sets is the kept set; support tokens are always attended."""
+    L, G, delta = 4096, 4, 3.0
+    q, K, V = _case(L, G, seed=33)
+    pk = orc.quantize_k(K)
+    r = {s: orc.decode_head(q, pk, V, L, delta, SCALE, select=s) for s in orc.SELECTIONS}
+    tu, tb, tt = r["union"]["tmask"], r["head_block"]["tmask"], r["head_token"]["tmask"]
+    assert (tt <= tb).all() and (tb <= tu).all()
+    assert tt.sum() < tb.sum() < tu.sum(), "case too easy: the variants coincide"
+    blocks_any = np.zeros((L + 63) // 64, bool)
+    for h in range(G):
+        blocks_any |= tb[h].reshape(-1, 64).any(axis=1)
+    np.testing.assert_array_equal(blocks_any, r["union"]["keep"])
+    sup = orc.support_mask(L, 64, 256)
+    assert tt[:, sup].all()
+    # within a kept block a head_token head attends exactly the tokens at or above its threshold
+    s_est, thr = r["head_token"]["s_est"], r["head_token"]["thr"]
+    np.testing.assert_array_equal(tt[:, ~sup], (s_est >= thr[:, None])[:, ~sup])
+
+
+def test_selection_variants_reduce_to_union_and_dense():
+    L = 2000
+    q, K, V = _case(L, 4, seed=41)
+    pk = orc.quantize_k(K)
+    dense = orc.decode_head(q, pk, V, L, math.inf, SCALE)["out"]
+    for s in orc.SELECTIONS:
+        np.testing.assert_allclose(orc.decode_head(q, pk, V, L, math.inf, SCALE, select=s)["out"], dense,
+                                   rtol=0, atol=1e-13)
+    # one query head per KV head: the head's block set is the kept set
+    for h in range(4):
+        a = orc.decode_head(q[h:h + 1], pk, V, L, 4.0, SCALE, select="head_block")
+        u = orc.decode_head(q[h:h + 1], pk, V, L, 4.0, SCALE)
+        np.testing.assert_array_equal(a["tmask"], u["tmask"])
+        np.testing.assert_array_equal(a["out"], u["out"])
+
+
+def test_selection_variants_monotone_in_delta():
+    L = 3000
+    q, K, V = _case(L, 4, seed=43)
+    pk = orc.quantize_k(K)
+    for s in ("head_block", "head_token"):
+        prev = None
+        for d in (0.5, 2.0, 5.0, 9.0):
+            t = orc.decode_head(q, pk, V, L, d, SCALE, select=s)["tmask"]
+            if prev is not None:
+                assert (prev <= t).all(), f"{s}: delta {d} drops tokens kept at a smaller delta"
+            prev = t
