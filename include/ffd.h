@@ -112,6 +112,9 @@ typedef struct ffd_cache {
  *  m_tilde       f32 [B][Hq]        pseudo-max per query head
  *  bmax          f32 [B][Hq][nblk]  largest estimated score per block (valid blocks only)
  *  keep          u8  [B][Hkv][nblk] 1 = block kept (valid blocks only)
+ *  tmask         u8  [B][Hq][max_seq_len]  1 = the query head attends the token,
+ *                0 = masked by the selection; written for the valid tokens of
+ *                kept blocks only (the rest of the array is left as it was)
  *  attend_start  hipEvent_t recorded on the stream right before the fused
  *  attend_stop   scan + refine kernel, and right after it
  *  stages        0 = the whole step; otherwise a bitmask of the launches to
@@ -125,7 +128,20 @@ typedef struct ffd_debug {
   void* attend_start;
   void* attend_stop;
   int32_t stages;
+  uint8_t* tmask;
 } ffd_debug_t;
+
+/* What each query head attends inside the blocks kept for its KV head (the
+ * blocks loaded and refined are the same in every case).
+ *  FFD_SELECT_UNION       every valid token of every kept block (the block
+ *                         filter of Method 3 stage 2, shared by the GQA group)
+ *  FFD_SELECT_HEAD_BLOCK  the kept blocks that hold a support token or whose
+ *                         largest estimated score reaches this head's own
+ *                         threshold m~[h] - delta
+ *  FFD_SELECT_HEAD_TOKEN  Method 2's criterion per token and head: the support
+ *                         tokens plus every token whose estimated score
+ *                         reaches this head's threshold */
+enum ffd_selection { FFD_SELECT_UNION = 0, FFD_SELECT_HEAD_BLOCK = 1, FFD_SELECT_HEAD_TOKEN = 2 };
 
 /* Bytes of each packed-cache field for `shape` (host call, no GPU work). */
 int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes,
@@ -188,6 +204,13 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
                     const int32_t* seq_lens, float delta, float sm_scale, void* out,
                     void* workspace, size_t workspace_bytes, const ffd_debug_t* debug,
                     void* stream);
+
+/* ffd_decode_attn with a selection variant (enum ffd_selection; any other
+ * value returns FFD_ERR_ARG).  ffd_decode_attn is this call with
+ * FFD_SELECT_UNION. */
+int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
+                           const int32_t* seq_lens, float delta, float sm_scale, int32_t selection, void* out,
+                           void* workspace, size_t workspace_bytes, const ffd_debug_t* debug, void* stream);
 
 /* Dense flash-decode attention over fp16 K and V ([B][Hkv][max_seq_len][128]),
  * the speed baseline: out = softmax(q k^T * sm_scale) v over tokens [0, L).

@@ -21,7 +21,7 @@ STATUS = {
 }
 EXPORTED = (
     "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
-    "ffd_decode_attn",
+    "ffd_decode_attn", "ffd_decode_attn_select",
     "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
 )
 
@@ -45,7 +45,10 @@ class Cache(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [("m_tilde", ctypes.c_void_p), ("bmax", ctypes.c_void_p), ("keep", ctypes.c_void_p),
-                ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p), ("stages", ctypes.c_int32)]
+                ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p), ("stages", ctypes.c_int32),
+                ("tmask", ctypes.c_void_p)]
+
+SELECTIONS = {"union": 0, "head_block": 1, "head_token": 2}
 
 
 _lib = None
@@ -67,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.ffd_append_kv.argtypes = [P(Shape), V, V, V, P(Cache), V]
         L.ffd_decode_attn.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, V, V, SZ,
                                       P(Debug), V]
+        L.ffd_decode_attn_select.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, I32, V,
+                                             V, SZ, P(Debug), V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
         L.ffd_strerror.argtypes = [ctypes.c_int]
         L.ffd_strerror.restype = ctypes.c_char_p
@@ -191,7 +196,9 @@ def append_kv(shape: Shape, k_new, v_new, pos, cache: PackedCache, stream=None) 
 
 
 def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,
-                workspace, debug: Optional[dict] = None, stream=None) -> None:
+                workspace, debug: Optional[dict] = None, stream=None, select: str = "union") -> None:
+    """One decode step; ``select`` is "union" (ffd_decode_attn) or a selection
+    variant "head_block" / "head_token" (ffd_decode_attn_select)."""
     import torch
     rows = shape.batch * shape.num_q_heads
     _need(q, torch.float16, rows * 128, "q")
@@ -205,11 +212,21 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
     dbg = None
     if debug is not None:
         dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
-                    debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)))
-    _check(lib().ffd_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
-                                 float(delta), float(sm_scale), _ptr(out), _ptr(workspace),
-                                 workspace.numel(), None if dbg is None else ctypes.byref(dbg),
-                                 _stream(stream)), "ffd_decode_attn")
+                    debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)),
+                    _ptr(debug.get("tmask")))
+    if select == "union":
+        _check(lib().ffd_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
+                                     float(delta), float(sm_scale), _ptr(out), _ptr(workspace),
+                                     workspace.numel(), None if dbg is None else ctypes.byref(dbg),
+                                     _stream(stream)), "ffd_decode_attn")
+    else:
+        if select not in SELECTIONS:
+            raise ValueError(f"unknown selection {select!r}")
+        _check(lib().ffd_decode_attn_select(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
+                                            float(delta), float(sm_scale), SELECTIONS[select], _ptr(out),
+                                            _ptr(workspace), workspace.numel(),
+                                            None if dbg is None else ctypes.byref(dbg), _stream(stream)),
+               "ffd_decode_attn_select")
 
 
 def dense_decode_attn(shape: Shape, q, k, v, seq_lens, sm_scale: float, out, workspace, stream=None) -> None:

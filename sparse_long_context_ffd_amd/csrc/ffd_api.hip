@@ -10,6 +10,10 @@
 #include "ffd_device.h"
 #include "ffd_launch.h"
 
+static_assert(ffd::kSelectUnion == FFD_SELECT_UNION && ffd::kSelectHeadBlock == FFD_SELECT_HEAD_BLOCK &&
+                  ffd::kSelectHeadToken == FFD_SELECT_HEAD_TOKEN,
+              "selection codes of the ABI and the kernels differ");
+
 
 namespace {
 
@@ -84,7 +88,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 extern "C" {
 
-int ffd_version(void) { return 300; }
+int ffd_version(void) { return 400; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -178,6 +182,13 @@ int ffd_append_kv(const ffd_shape_t* shape, const void* k_new, const void* v_new
 int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
                     float delta, float sm_scale, void* out, void* workspace, size_t workspace_bytes,
                     const ffd_debug_t* debug, void* stream) {
+  return ffd_decode_attn_select(shape, q, cache, seq_lens, delta, sm_scale, FFD_SELECT_UNION, out, workspace,
+                                workspace_bytes, debug, stream);
+}
+
+int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
+                           const int32_t* seq_lens, float delta, float sm_scale, int32_t selection, void* out,
+                           void* workspace, size_t workspace_bytes, const ffd_debug_t* debug, void* stream) {
   const int st = check_shape(shape);
   if (st) return st;
   if (!q || !cache || !seq_lens || !out || !cache->codes || !cache->sz || !cache->res || !cache->rscale ||
@@ -189,11 +200,14 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
     return FFD_ERR_ALIGN;
   if (isnan(delta) || (isinf(delta) && delta < 0)) return FFD_ERR_DELTA;
   if (!(sm_scale > 0.f) || isinf(sm_scale)) return FFD_ERR_ARG;
+  if (selection != FFD_SELECT_UNION && selection != FFD_SELECT_HEAD_BLOCK && selection != FFD_SELECT_HEAD_TOKEN)
+    return FFD_ERR_ARG;
   const Plan pl = make_plan(shape);
   if (!workspace || workspace_bytes < pl.total) return FFD_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FFD_ERR_ALIGN;
 
   ffd::DecodeParams p = {};
+  p.select = selection;
   char* ws = static_cast<char*>(workspace);
   p.q = static_cast<const uint16_t*>(q);
   p.codes = static_cast<const uint8_t*>(cache->codes);
@@ -211,6 +225,7 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
     p.dbg_mt = debug->m_tilde;
     p.dbg_bmax = debug->bmax;
     p.dbg_keep = debug->keep;
+    p.dbg_tmask = debug->tmask;
     p.ev_start = static_cast<hipEvent_t>(debug->attend_start);
     p.ev_stop = static_cast<hipEvent_t>(debug->attend_stop);
   }

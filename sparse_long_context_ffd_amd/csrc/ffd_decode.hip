@@ -49,6 +49,16 @@ __device__ inline float quad_sum(float v) {
   return v;
 }
 
+// ballot over a tile's lanes -> bit hc set when some lane of head column hc
+// (lanes with (lane & 15) >> 2 == hc, any row group) voted
+__device__ inline uint32_t head_bits(uint64_t bal) {
+  uint32_t x = (uint32_t)bal | (uint32_t)(bal >> 32);
+  x = (x | (x >> 16)) & 0xffffu;
+  x |= x >> 1;
+  x |= x >> 2;
+  return (x & 1u) | ((x >> 3) & 2u) | ((x >> 6) & 4u) | ((x >> 9) & 8u);
+}
+
 // 2-bit code word -> MFMA A fragment of 8 fp16 values 4 + c (channels j = 0..7):
 // the code lands in mantissa bits 8-9 of an fp16 with exponent 2 (ulp 1/4)
 constexpr uint32_t kCodeMask = 0x03000300u, kOneHalf2 = 0x44004400u;
@@ -542,7 +552,7 @@ struct RefineRegs {
 
 // Register budget: 3 waves per SIMD for G <= 4 (<= 168 VGPRs, no spills); the
 // G > 4 variant keeps twice the accumulators and runs at 2.
-template <int G>
+template <int G, int SEL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void attend_kernel(
     DecodeParams p) {
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
@@ -589,7 +599,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __shared__ uint32_t qs[G * 64];
   __shared__ float pm_s[256];
   QFrags<G>::stage_store(qst, tid, qs);
-  __shared__ int kflag[kWaves][CBMAX];  // wave's tile of block j reached a threshold
+  // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
+  // h) under the per-head block selection
+  __shared__ int kflag[kWaves][CBMAX];
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
   float* est = dyn;                                                // [cb][kWaves][G][16]
@@ -643,11 +655,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
             for (int i = 0; i < 4; ++i) e[nt][i] = (row0 + i < L) ? e[nt][i] : -INFINITY;
         }
+        // per-head block selection: bit h = head h reaches its threshold in
+        // this tile; otherwise one flag for the group
+        uint32_t hreach = 0;
         bool reach = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           const float mx = fmaxf(fmaxf(e[nt][0], e[nt][1]), fmaxf(e[nt][2], e[nt][3]));
-          reach = reach || (mx >= thr[nt]);
+          if constexpr (SEL == kSelectHeadBlock)
+            hreach |= head_bits(__builtin_amdgcn_ballot_w64(mx >= thr[nt])) << (4 * nt);
+          else
+            reach = reach || (mx >= thr[nt]);
           const int h = 4 * nt + hc;
           if (gc == 0 && h < G) {
             *reinterpret_cast<float4*>(&est[((j * kWaves + wave) * G + h) * 16 + 4 * ks]) =
@@ -655,8 +673,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
             if (dbg_bmax) tmax[(j * 4 * kWaves + 4 * wave + ks) * G + h] = mx;
           }
         }
-        const bool any = __builtin_amdgcn_ballot_w64(reach) != 0;
-        if (lane == 0) kflag[wave][j] = any ? 1 : 0;
+        if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
+        if (lane == 0) kflag[wave][j] = (int)hreach;
       }
     }
   };
@@ -675,13 +693,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __syncthreads();
 
   // ---- block decisions (every wave derives the same mask) ----
+  // forced blocks: [0, sink_end) and [local_beg, nblk)
+  const int sink_end = p.sink > 0 ? ((min(p.sink, L) + 63) >> 6) : 0;
+  const int local_beg = p.local > 0 ? (max(0, L - p.local) >> 6) : nblk;
   uint64_t kmask;
   {
     bool kp = false;
     if (lane < nbl) {
       const int blk = blk0 + lane;
-      const int sink_end = p.sink > 0 ? ((min(p.sink, L) + 63) >> 6) : 0;
-      const int local_beg = p.local > 0 ? (max(0, L - p.local) >> 6) : nblk;
       kp = blk < sink_end || blk >= local_beg || kflag[0][lane] || kflag[1][lane] || kflag[2][lane] ||
            kflag[3][lane];
       if (wave == 0) {
@@ -719,20 +738,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
     };
     const float c2 = p.sm_scale * kLog2e, slack = 8.f / c2;
+    // support tokens [0, sup_lo) and [sup_hi, L) (always attended per token)
+    const int sup_lo = min(p.sink, L), sup_hi = max(0, L - p.local);
     auto refine = [&](int j, RefineRegs& x) {
-      const int n_rows = min(16, L - ((blk0 + j) * 64 + 16 * wave));
+      const int tok0 = (blk0 + j) * 64 + 16 * wave;  // first row of the wave's tile
+      const int n_rows = min(16, L - tok0);
       if (n_rows <= 0) return;  // this wave's tile lies past the sequence end
       float xs[NT][4];
       qf.residual(x.R, x.S8, xs);
+      // heads that attend this block under the per-head block selection
+      uint32_t hb = ~0u;
+      if constexpr (SEL == kSelectHeadBlock) {
+        const int blk = blk0 + j;
+        if (blk >= sink_end && blk < local_beg) hb = kflag[0][j] | kflag[1][j] | kflag[2][j] | kflag[3][j];
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int h = 4 * nt + hc;
         const int hh = h < G ? h : 0;
         const float4 e4 = *reinterpret_cast<const float4*>(&est[((j * kWaves + wave) * G + hh) * 16 + 4 * ks]);
-        xs[nt][0] += e4.x;
-        xs[nt][1] += e4.y;
-        xs[nt][2] += e4.z;
-        xs[nt][3] += e4.w;
+        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bool att = true;
+          if constexpr (SEL == kSelectHeadBlock) att = (hb >> hh) & 1u;
+          if constexpr (SEL == kSelectHeadToken) {
+            const int t = tok0 + 4 * ks + i;
+            att = t < sup_lo || t >= sup_hi || ev[i] >= thr[nt];
+          }
+          xs[nt][i] = att ? xs[nt][i] + ev[i] : -INFINITY;
+        }
       }
       if (n_rows < 16) {  // rows past the end: -inf scores, zero values (their bytes may be anything)
         const int r0 = 4 * ks;
@@ -748,6 +783,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
           x.V[q].y &= m23;
           x.V[q].z &= m01;
           x.V[q].w &= m23;
+        }
+      }
+      if (p.dbg_tmask) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int h = 4 * nt + hc;
+          if (gc == 0 && h < G)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * ks + i < n_rows)
+                p.dbg_tmask[((size_t)b * p.Hq + qh0 + h) * p.L_cap + tok0 + 4 * ks + i] =
+                    xs[nt][i] != -INFINITY ? 1 : 0;
         }
       }
       h4 va[8];
@@ -929,6 +976,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
+template <int G, int SEL>
+static void launch_attend(const DecodeParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((attend_kernel<G, SEL>), dim3(p.nchunk, p.Hkv, p.B), dim3(256), AttendCfg<G>::lds_bytes(p.cb),
+                     s, p);
+}
 template <int G>
 static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
   const int stages = p.stages ? p.stages : 7;
@@ -936,8 +988,12 @@ static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL(pseudomax_kernel<G>, dim3(p.npart, p.Hkv, p.B), dim3(256), 0, s, p);
   if (stages & 2) {
     if (p.ev_start) (void)hipEventRecord(p.ev_start, s);
-    hipLaunchKernelGGL(attend_kernel<G>, dim3(p.nchunk, p.Hkv, p.B), dim3(256), AttendCfg<G>::lds_bytes(p.cb), s,
-                       p);
+    if (p.select == kSelectHeadBlock)
+      launch_attend<G, kSelectHeadBlock>(p, s);
+    else if (p.select == kSelectHeadToken)
+      launch_attend<G, kSelectHeadToken>(p, s);
+    else
+      launch_attend<G, kSelectUnion>(p, s);
     if (p.ev_stop) (void)hipEventRecord(p.ev_stop, s);
   }
   if (stages & 4) hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);

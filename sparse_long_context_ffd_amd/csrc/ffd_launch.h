@@ -6,6 +6,11 @@
 
 namespace ffd {
 
+// what each query head attends inside the kept blocks
+constexpr int kSelectUnion = 0;      // every valid token
+constexpr int kSelectHeadBlock = 1;  // forced blocks and blocks reaching the head's own threshold
+constexpr int kSelectHeadToken = 2;  // support tokens and tokens reaching the head's own threshold
+
 struct DecodeParams {
   const uint16_t* q;       // [B][Hq][128] fp16
   const uint8_t* codes;    // packed cache fields (layouts in include/ffd.h)
@@ -21,10 +26,12 @@ struct DecodeParams {
   float* dbg_mt;           // optional [B][Hq]
   float* dbg_bmax;         // optional [B][Hq][nblk_cap]
   uint8_t* dbg_keep;       // optional [B][Hkv][nblk_cap]
+  uint8_t* dbg_tmask;      // optional [B][Hq][L_cap]: token attended by the head (kept blocks only)
   uint16_t* out;           // [B][Hq][128] fp16
   hipEvent_t ev_start;     // optional, recorded around the attend kernel
   hipEvent_t ev_stop;
   int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge
+  int select;              // kSelectUnion / kSelectHeadBlock / kSelectHeadToken
   int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
   float delta, sm_scale;
 };

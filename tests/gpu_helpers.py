@@ -68,7 +68,7 @@ def cache_to_host(cache):
     return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
-def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None):
+def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union"):
     import sparse_long_context_ffd_amd as ffd
     B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
     nb = shape.max_seq_len // 64
@@ -79,8 +79,9 @@ def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, w
         "m_tilde": torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda"),
         "bmax": torch.full((B, Hq, nb), float("nan"), dtype=torch.float32, device="cuda"),
         "keep": torch.full((B, Hkv, nb), 7, dtype=torch.uint8, device="cuda"),
+        "tmask": torch.full((B, Hq, shape.max_seq_len), 7, dtype=torch.uint8, device="cuda"),
     }
-    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg)
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg, select=select)
     torch.cuda.synchronize()
     return {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
 
@@ -103,8 +104,14 @@ def mask_pins(o):
 
 
 def check_head(orc, q16, pk_head, V16, L, delta, got, b, h, G, sink=64, local=256, sm_scale=SM_SCALE,
-               label=""):
-    """Compare one (b, kv head) of a GPU decode with the oracle; returns stats."""
+               label="", select="union"):
+    """Compare one (b, kv head) of a GPU decode with the oracle; returns stats.
+
+    The per-head token decisions of a selection variant (debug ``tmask``) must
+    equal the oracle's wherever they are pinned -- support tokens, forced
+    blocks, and estimates or block maxima farther than BAND from the head's
+    threshold -- and the output is compared with the oracle evaluated under
+    the GPU's block mask and token decisions."""
     nb = (L + 63) // 64
     o = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local)
     keep = got["keep"][b, h, :nb].astype(bool)
@@ -120,7 +127,26 @@ def check_head(orc, q16, pk_head, V16, L, delta, got, b, h, G, sink=64, local=25
     bm_err = float(np.abs(bm - o["bmax"]).max())
     assert mt_err <= BAND, f"{label} pseudo-max error {mt_err}"
     assert bm_err <= BAND, f"{label} block-max error {bm_err}"
-    ref = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local, keep=keep)["out"]
+    tmask = None
+    if "tmask" in got:
+        tok = np.repeat(keep, 64)[:L]
+        tm = got["tmask"][b, h * G:(h + 1) * G, :L]
+        assert set(np.unique(tm[:, tok]).tolist()) <= {0, 1}, f"{label} token flags not 0/1"
+        want = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local, keep=keep,
+                               select=select)["tmask"]
+        thr = o["thr"][:, None]
+        if select == "union":
+            pinned = np.ones((G, L), bool)
+        elif select == "head_block":
+            pb = o["forced"][None, :] | (np.abs(o["bmax"] - thr) > BAND)
+            pinned = np.repeat(pb, 64, axis=1)[:, :L]
+        else:
+            pinned = orc.support_mask(L, sink, local)[None, :] | (np.abs(o["s_est"] - thr) > BAND)
+        pinned &= tok[None, :]
+        bad = np.argwhere(pinned & ((tm == 1) != want))
+        assert bad.size == 0, f"{label} {select}: token decisions differ at (head, token) {bad[:8].tolist()}"
+        tmask = (tm == 1) & tok[None, :]
+    ref = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local, keep=keep, tmask=tmask)["out"]
     g_out = got["out"][b, h * G:(h + 1) * G]
     d = g_out - ref
     max_abs = float(np.abs(d).max())
@@ -129,4 +155,5 @@ def check_head(orc, q16, pk_head, V16, L, delta, got, b, h, G, sink=64, local=25
     assert max_abs <= ATOL and rel <= RTOL_L2, f"{label} output max-abs {max_abs} rel-L2 {rel}"
     return {"keep_frac": float(keep.mean()), "exempt": int(nb - pk.sum() - pd.sum()),
             "mt_err": mt_err, "bmax_err": bm_err, "max_abs": max_abs, "rel_l2": rel, "rmse": rmse,
-            "mask_equal": bool((keep == o["keep"]).all())}
+            "mask_equal": bool((keep == o["keep"]).all()),
+            "attended_frac": None if tmask is None else float(tmask.mean())}

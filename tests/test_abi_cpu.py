@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 300
+    assert L.ffd_version() == 400
 
 
 def test_strerror_covers_codes():
@@ -91,6 +91,22 @@ def test_decode_argument_errors():
     assert _decode(s, wsb=_ws(s) - 1) == -5
     assert _decode(s, ws=None) == -5
     assert _decode(s, ws=FAKE + 8) == -3
+
+
+def _decode_sel(shape, selection, q=FAKE, ws=FAKE):
+    c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return ffd.lib().ffd_decode_attn_select(ctypes.byref(shape), q, ctypes.byref(c), FAKE, 5.0, 0.088, selection,
+                                            FAKE, ws, _ws(shape), None, None)
+
+
+def test_decode_select_argument_errors():
+    s = ffd.make_shape(1, 32, 8, 16384)
+    for bad in (-1, 3, 7, 1 << 20):
+        assert _decode_sel(s, bad) == -6, bad
+    for sel in (0, 1, 2):                       # valid codes still validate the rest first
+        assert _decode_sel(s, sel, q=None) == -1
+        assert _decode_sel(s, sel, ws=FAKE + 8) == -3
+    assert set(_lib.SELECTIONS.values()) == {0, 1, 2}
 
 
 def test_dense_and_pack_argument_errors():

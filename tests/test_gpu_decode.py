@@ -16,7 +16,7 @@ from tests.gpu_helpers import (SM_SCALE, cache_to_host, check_head, dev, gpu_dec
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, seed, deltas, heads=None, chunk_blocks=0, sink=None, local=None, fill=0xFF):
+def _run(w, seed, deltas, heads=None, chunk_blocks=0, sink=None, local=None, fill=0xFF, select="union"):
     torch = torch_mod()
     c = make_case(w, seed, heads=heads)
     shape = shape_for(w, chunk_blocks, sink, local)
@@ -29,13 +29,14 @@ def _run(w, seed, deltas, heads=None, chunk_blocks=0, sink=None, local=None, fil
     todo = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
     stats = []
     for delta in deltas:
-        say(f"decode {w.name} seed={seed} delta={delta} cb={chunk_blocks} sink={S} local={W} heads={todo}")
-        got = gpu_decode(shape, qd, cache, ld, delta, torch)
+        say(f"decode {w.name} seed={seed} delta={delta} cb={chunk_blocks} sink={S} local={W} select={select} "
+            f"heads={todo}")
+        got = gpu_decode(shape, qd, cache, ld, delta, torch, select=select)
         for b, h in todo:
             L = int(c["seq_lens"][b])
             pk = orc.quantize_k(c["k"][b, h])
             st = check_head(orc, c["q"][b, h * G:(h + 1) * G], pk, c["v"][b, h], L, delta, got, b, h, G,
-                            sink=S, local=W, label=f"{w.name} s{seed} d{delta} b{b} h{h}")
+                            sink=S, local=W, label=f"{w.name} s{seed} d{delta} b{b} h{h}", select=select)
             st.update(delta=delta, b=b, h=h)
             stats.append(st)
     for s in stats:
