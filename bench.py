@@ -118,7 +118,7 @@ def prepare(w, seed, torch):
     return c, {k: to_dev(v, torch) for k, v in c.items()}
 
 
-def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
+def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=False):
     import sparse_long_context_ffd_amd as ffd
     shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
     base = ffd.PackedCache(shape)
@@ -149,9 +149,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     layers = [base] + [base.clone() for _ in range(R - 1)]
     log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
 
-    def step(i, stages=0):
+    def step(i, stages=0, select="union"):
         ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
-                        debug={"stages": stages} if stages else None)
+                        debug={"stages": stages} if stages else None, select=select)
 
     # eager launches (host-bound for short contexts), for reference
     for i in range(warmup):
@@ -193,7 +193,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
     loop_total_ms = timed_replay(g_loop, torch)
     us_step = total_ms * 1e3 / steps
     attend_us = attend_total_ms * 1e3 / steps
+    variants = selection_variants(shape, w, delta, d, base, ws, sm_scale, torch, steps, step) if with_variants else None
     return {
+        "variants": variants,
         "us_per_step": us_step,
         "wall_us_per_step": wall * 1e6 / steps,
         "eager_us_per_step": eager_us,
@@ -206,6 +208,36 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale):
         "layers_rotated": R,
         "plan": ffd.plan(shape),
     }
+
+
+def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, step):
+    """Per-head block sets and per-token masking: time per step, fraction of
+    (query head, token) pairs attended, and the output's deviation from full
+    attention over K-hat (delta = +inf) -- the bytes loaded are the kept
+    blocks' in every variant."""
+    import sparse_long_context_ffd_amd as ffd
+    rows = (w.batch, w.q_heads, 128)
+    full = torch.empty(rows, dtype=torch.float16, device="cuda")
+    ffd.decode_attn(shape, d["q"], cache, d["seq_lens"], math.inf, sm_scale, full, ws)
+    lens = d["seq_lens"].long()
+    valid = torch.arange(w.max_len, device="cuda")[None, :] < lens[:, None]          # [B][L_cap]
+    res = {}
+    for sel in ("union", "head_block", "head_token"):
+        o = torch.empty(rows, dtype=torch.float16, device="cuda")
+        tm = torch.zeros((w.batch, w.q_heads, w.max_len), dtype=torch.uint8, device="cuda")
+        ffd.decode_attn(shape, d["q"], cache, d["seq_lens"], delta, sm_scale, o, ws, debug={"tmask": tm},
+                        select=sel)
+        torch.cuda.synchronize()
+        att = ((tm == 1) & valid[:, None, :]).sum().item() / (valid.sum().item() * w.q_heads)
+        diff = (o.float() - full.float())
+        g = graph_of([lambda i=i: step(i, select=sel) for i in range(steps)], torch)
+        g.replay()
+        us = timed_replay(g, torch) * 1e3 / steps
+        res[sel] = {"us_per_step": round(us, 3), "attended_frac": round(att, 5),
+                    "max_abs_vs_full": round(diff.abs().max().item(), 6),
+                    "rel_l2_vs_full": round((diff.norm() / full.float().norm()).item(), 6)}
+        del g
+    return res
 
 
 def measure_dense(w, steps, warmup, d, torch, sm_scale):
@@ -296,7 +328,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     c, d = prepare(w, args.seed, torch)
-    r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale)
+    r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale, with_variants=True)
     dense = measure_dense(w, args.steps, args.warmup, d, torch, sm_scale)
     achieved = r["attend_bytes"] / (r["attend_us_mean"] * 1e3)
     result = {
@@ -320,6 +352,7 @@ def main():
         "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
         "attend_kernel_us": round(r["attend_us_mean"], 3),
         "decode_loop_us_per_step": round(r["loop_us_per_step"], 3),
+        "selection_variants": r["variants"],
         "dense_us_per_step": round(dense["us_per_step"], 3),
         "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -13,8 +13,8 @@
 // double rounding to differ from rounding the exact quotient).
 //
 // Launch: grid (ceil(n/64), Hkv, B), 256 threads; thread = (token, group),
-// 4 threads per token, 64 tokens per work-group.  The decode-loop append runs
-// the same per-group quantizer for one token per (sequence, KV head).
+// 4 threads per token, 64 tokens per work-group.  The decode-loop append takes
+// the same decisions for one token per (sequence, KV head), spread over a wave.
 #include "ffd_device.h"
 #include "ffd_launch.h"
 
@@ -161,11 +161,19 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 
 // Decode-loop append: one new token per (sequence, KV head), written at the
 // sequence's own position pos[b] read on the device (so the append can sit in a
-// captured graph beside the decode step).  One wave per (b, kv head): lanes
-// 0..3 quantize the four groups of the key (every lane computes group lane & 3
-// so that the code-word exchange has both partners; lanes >= 4 store nothing);
-// lane = channel pair for the value, stored into the token-quad tiled layout.
-// A position outside [0, L_cap) skips the sequence.
+// captured graph beside the decode step).  One wave per (b, kv head); lane l
+// owns channels 2l and 2l+1 of the key (group l / 16) and of the value.  The
+// decisions are those of pack_group, spread over the lanes: group minimum,
+// maximum and largest residual by exact reductions over the group's 16 lanes,
+// scales by the same roundings, codes and residual bytes per channel.  A
+// position outside [0, L_cap) skips the sequence.
+__device__ inline double shfl_xor_f64(double v, int m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)u, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), m, 64);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__ k_new,
                                                     const uint16_t* __restrict__ v_new,
                                                     const int32_t* __restrict__ pos, int L_cap,
@@ -177,8 +185,66 @@ __global__ __launch_bounds__(64) void append_kernel(const uint16_t* __restrict__
   const size_t head = (size_t)b * gridDim.x + blockIdx.x;
   const int t = pos[b];
   if (t < 0 || t >= L_cap) return;  // uniform over the work-group
-  const int g = lane & 3;
-  pack_group(k_new + head * kHeadDim + g * kGroup, head, L_cap >> 6, t, g, lane < 4, codes, sz, res, rsc);
+  const int g = lane >> 4, li = lane & 15;
+  const uint32_t kw = *reinterpret_cast<const uint32_t*>(k_new + head * kHeadDim + 2 * lane);
+  const double x[2] = {f16bits_to_f64((uint16_t)(kw & 0xffffu)), f16bits_to_f64((uint16_t)(kw >> 16))};
+  double mn = fmin(x[0], x[1]), mx = fmax(x[0], x[1]);
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+    mn = fmin(mn, shfl_xor_f64(mn, m));
+    mx = fmax(mx, shfl_xor_f64(mx, m));
+  }
+  mn = mn + 0.0;  // -0 -> +0
+  const uint16_t zb = f64_to_f16_rne(mn);
+  const uint16_t sb = f64_to_f16_rne((mx - mn) / 3.0 + 0.0);
+  const double s = f16bits_to_f64(sb);
+  int c[2];
+  double r[2], amax = 0.0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const double d = x[i] - mn;
+    c[i] = s > 0.0 ? (d >= 0.5 * s) + (d >= 1.5 * s) + (d >= 2.5 * s) : 0;
+    r[i] = x[i] - (mn + c[i] * s);  // exact
+    amax = fmax(amax, fabs(r[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) amax = fmax(amax, shfl_xor_f64(amax, m));
+  const uint16_t s8b = f64_to_f16_rne(amax / 127.0);
+  const double s8 = f16bits_to_f64(s8b);
+  int e[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    e[i] = 0;
+    if (s8 > 0.0) {
+      const double a = fabs(r[i]);
+      double kf = floor(a / s8 + 0.5);
+      if (a >= (kf + 0.5) * s8) kf += 1.0;
+      if (kf > 0.0 && a < (kf - 0.5) * s8) kf -= 1.0;
+      kf = fmin(kf, 127.0);
+      e[i] = (int)kf;
+      if (r[i] < 0.0) e[i] = -e[i];
+    }
+  }
+  // code word (kq, p) holds channels 8kq..8kq+7 of groups 2p and 2p+1: the
+  // lanes 32p + 4kq + {0..3} and 16 lanes above them
+  const int kq = li >> 2, j0 = 2 * (li & 3);
+  uint32_t bits = ((uint32_t)c[0] << code_bit(g, j0)) | ((uint32_t)c[1] << code_bit(g, j0 + 1));
+  bits |= (uint32_t)__shfl_xor((int)bits, 1, 64);
+  bits |= (uint32_t)__shfl_xor((int)bits, 2, 64);
+  bits |= (uint32_t)__shfl_xor((int)bits, 16, 64);
+
+  const int blk = t >> 6, tb = t & 63;
+  const size_t blk_idx = head * (size_t)(L_cap >> 6) + blk;
+  if ((lane & 0x13) == 0)
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(codes) + blk_idx * kCodesBytes +
+                                 codes_word_off(tb, kq, g >> 1)) = bits;
+  if (li == 0) {
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sz) + blk_idx * kSzBytes + sz_off(tb, g)) =
+        (uint32_t)sb | ((uint32_t)zb << 16);
+    *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(rsc) + blk_idx * kRscBytes + rsc_off(tb, g)) = s8b;
+  }
+  *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(res) + blk_idx * kResBytes + res_off(tb, 2 * lane)) =
+      (uint16_t)((uint32_t)(e[0] & 0xff) | ((uint32_t)(e[1] & 0xff) << 8));
   const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_new + head * kHeadDim + 2 * lane);
   uint16_t* dst = vt + (head * L_cap + (size_t)(t & ~3)) * kHeadDim + 8 * lane + (t & 3);
   dst[0] = (uint16_t)(vv & 0xffffu);  // channel 2*lane
