@@ -254,3 +254,29 @@ def test_decode_loop_append_and_decode_in_one_graph():
                 pk = orc.quantize_k(K[b, h])
                 check_head(orc, qn[b, h * G:(h + 1) * G], pk, V[b, h], int(L[b]), 5.0, got, b, h, G,
                            label=f"loop step {i} b{b} h{h}")
+
+
+def test_dense_workspace_reuse_and_ragged_rows():
+    """Dense calls in a row on one workspace with lengths that change the
+    number of chunks per row between calls each match the oracle (nothing a
+    call leaves in the workspace leaks into the next)."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    w = Workload("dense_reuse", 3, 12, 3, 2048, None, len_range=(1, 2048))
+    c = make_case(w, 4)
+    shape = shape_for(w, chunk_blocks=2)
+    ws = torch.full((ffd.workspace_bytes(shape),), 0x7F, dtype=torch.uint8, device="cuda")
+    qd, kd, vd = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
+    G = w.group
+    for r, lens in enumerate(([2048, 1, 700], [64, 2047, 129], [1000, 1000, 1000])):
+        say(f"dense reuse call {r} lens {lens}")
+        ld = dev(np.array(lens, np.int32), torch)
+        out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+        ffd.dense_decode_attn(shape, qd, kd, vd, ld, SM_SCALE, out, ws)
+        got = out.float().cpu().numpy()
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                ref = orc.dense_head(c["q"][b, h * G:(h + 1) * G], c["k"][b, h], c["v"][b, h], lens[b], SM_SCALE)
+                d = got[b, h * G:(h + 1) * G] - ref
+                assert np.abs(d).max() <= 2e-3 and np.linalg.norm(d) <= 1e-3 * np.linalg.norm(ref), \
+                    f"call {r} b{b} h{h}"
