@@ -208,6 +208,7 @@ int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_ca
 
   ffd::DecodeParams p = {};
   p.select = selection;
+  p.interleaved = 1;
   char* ws = static_cast<char*>(workspace);
   p.q = static_cast<const uint16_t*>(q);
   p.codes = static_cast<const uint8_t*>(cache->codes);

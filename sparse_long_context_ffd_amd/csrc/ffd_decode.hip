@@ -24,7 +24,8 @@
 //              C = q_g . e_g;      exact = est + rscale*C
 //
 // Work decomposition of attend/dense: one work-group (4 wave64) per chunk of `cb`
-// 64-token blocks of one (sequence, KV head).  Wave w owns token tile
+// 64-token blocks of one (sequence, KV head) -- contiguous blocks for dense,
+// interleaved over the sequence (stride = number of chunks) for attend.  Wave w owns token tile
 // [16w, 16w+16) of every block of the chunk, so the four waves do identical work
 // and each keeps its own online-softmax state; the states are combined in LDS
 // into one partial per chunk, which merge_kernel combines.
@@ -559,12 +560,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
   const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
-  const int blk0 = chunk * p.cb;
-  const int nbl_cap = min(p.cb, p.nblk_cap - blk0);
+  // the chunk's blocks are interleaved over the sequence: block j of chunk c
+  // is c + j * nchunk, so the always-kept sink and local-window blocks (and
+  // any cluster of kept blocks) spread over many work-groups
+  const int nck = p.nchunk;
+  auto blk_of = [&](int j) { return chunk + j * nck; };
+  const int nbl_cap = min(p.cb, (p.nblk_cap - chunk + nck - 1) / nck);
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
   const TileOffsets to(wave, lane);
-  const size_t bi0 = head * p.nblk_cap + blk0;
   // per-head buffer descriptors; lane offsets in VGPRs, block offsets in SGPRs
   const size_t hb = head * p.nblk_cap;  // first block of the head
   const uint32_t nbc = (uint32_t)p.nblk_cap;
@@ -581,8 +585,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int jj = min(j0 + v, nbl_cap - 1);
-      cw[v] = buf_load_b64(r_codes, (uint32_t)to.codes, (uint32_t)(blk0 + jj) * kCodesBytes);
-      zw[v] = buf_load_b128(r_sz, (uint32_t)to.sz, (uint32_t)(blk0 + jj) * kSzBytes);
+      cw[v] = buf_load_b64(r_codes, (uint32_t)to.codes, (uint32_t)blk_of(jj) * kCodesBytes);
+      zw[v] = buf_load_b128(r_sz, (uint32_t)to.sz, (uint32_t)blk_of(jj) * kSzBytes);
     }
   };
   load_batch(0, cwA, zwA);
@@ -611,8 +615,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
-  if (blk0 >= nblk) return;
-  const int nbl = min(p.cb, nblk - blk0);
+  if (chunk >= nblk) return;
+  const int nbl = min(p.cb, (nblk - chunk + nck - 1) / nck);
   const bool dbg_bmax = p.dbg_bmax != nullptr;
   // Drain every load issued so far (first batch, q, the pseudo-max parts) so
   // that the pipelined scan below starts from an exact count of loads in flight.
@@ -648,8 +652,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       if (j < nbl) {
         float e[NT][4];
         qf.estimate(cw[v], zw[v], e);
-        if ((blk0 + j + 1) * 64 > L) {
-          const int row0 = (blk0 + j) * 64 + 16 * wave + 4 * ks;
+        if ((blk_of(j) + 1) * 64 > L) {
+          const int row0 = blk_of(j) * 64 + 16 * wave + 4 * ks;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -700,7 +704,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   {
     bool kp = false;
     if (lane < nbl) {
-      const int blk = blk0 + lane;
+      const int blk = blk_of(lane);
       kp = blk < sink_end || blk >= local_beg || kflag[0][lane] || kflag[1][lane] || kflag[2][lane] ||
            kflag[3][lane];
       if (wave == 0) {
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
     const __amdgpu_buffer_rsrc_t r_v = make_rsrc(p.v + head * p.L_cap * kHeadDim, nbc * kVBytes);
     auto load_block = [&](int j, RefineRegs& x) {
-      const uint32_t blk = (uint32_t)(blk0 + j);
+      const uint32_t blk = (uint32_t)blk_of(j);
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
       x.S8 = buf_load_b64(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     // support tokens [0, sup_lo) and [sup_hi, L) (always attended per token)
     const int sup_lo = min(p.sink, L), sup_hi = max(0, L - p.local);
     auto refine = [&](int j, RefineRegs& x) {
-      const int tok0 = (blk0 + j) * 64 + 16 * wave;  // first row of the wave's tile
+      const int tok0 = blk_of(j) * 64 + 16 * wave;  // first row of the wave's tile
       const int n_rows = min(16, L - tok0);
       if (n_rows <= 0) return;  // this wave's tile lies past the sequence end
       float xs[NT][4];
@@ -749,7 +753,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       // heads that attend this block under the per-head block selection
       uint32_t hb = ~0u;
       if constexpr (SEL == kSelectHeadBlock) {
-        const int blk = blk0 + j;
+        const int blk = blk_of(j);
         if (blk >= sink_end && blk < local_beg) hb = kflag[0][j] | kflag[1][j] | kflag[2][j] | kflag[3][j];
       }
 #pragma unroll
@@ -929,7 +933,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const float2* ml = p.part_ml + row * p.nchunk;
   const float* po = p.part_o + row * p.nchunk * kHeadDim + ch;
   const int L = clamp_len(p, b);
-  const int nch = (((L + 63) >> 6) + p.cb - 1) / p.cb;
+  // chunks holding blocks of the sequence: the first ceil(nblk / cb) when
+  // chunks are contiguous (dense), every chunk below nblk when interleaved
+  const int nblk = (L + 63) >> 6;
+  const int nch = p.interleaved ? min(p.nchunk, nblk) : (nblk + p.cb - 1) / p.cb;
   float M = -INFINITY, o = 0.f, ls = 0.f;
   for (int c0 = 0; c0 < nch; c0 += kPiece) {
     const int n = min(kPiece, nch - c0);
