@@ -52,8 +52,8 @@ ROTATE_TARGET = 1.5e9
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "2c1ca7f2adce5872", "fetch": 9907.29, "write": 666.26},
-    "long_256k": {"sources": "2c1ca7f2adce5872", "fetch": 134914.46, "write": 3323.98},
+    "llama8b_16k": {"sources": "cc328da1ecaaa2f5", "fetch": 9917.75, "write": 329.84},
+    "long_256k": {"sources": "cc328da1ecaaa2f5", "fetch": 134979.16, "write": 1437.76},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
