@@ -272,6 +272,85 @@ def decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: 
             "bmax": bmax, "forced": forced, "keep": keep, "selected": sel, "tmask": tmask, "out": out}
 
 
+# --------------------------------------------------------------------------
+# run-time termination of the refine stream (the ART page, "Attention
+# Run-time Termination", Method sections 2.2-2.4), applied to each chunk
+# --------------------------------------------------------------------------
+ART_PROBE = 8  # probe = the first 8 output channels of the group's first query head
+
+
+def chunk_blocks(nblk: int, cb: int, nchunk: int) -> List[List[int]]:
+    """Blocks of each chunk under the interleaved split: chunk c holds blocks
+    c, c + nchunk, c + 2 nchunk, ... (at most cb of them, all below nblk)."""
+    return [[c + j * nchunk for j in range(cb) if c + j * nchunk < nblk] for c in range(min(nchunk, nblk))]
+
+
+def art_decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: int,
+                    delta: float, sm_scale: float, cb: int, nchunk: int, tau: float, phi: float,
+                    patience: int, sink: int = 64, local: int = 256,
+                    keep: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """FFD decode where every chunk's stream of kept blocks may stop early.
+
+    Each chunk (the unit that streams blocks into one running output) visits
+    its kept blocks in increasing order.  After block t it takes the probe
+    x_t = the first ART_PROBE channels of its running normalised output for
+    the group's first query head, and from the second block on compares it
+    with the previous probe:
+        d_scale = | ||x_t|| - ||x_{t-1}|| |,   d_dir = 1 - cos(x_t, x_{t-1})
+    (d_dir = 1 when either norm is 0).  A step is stable when d_scale < tau
+    and d_dir < phi; after `patience` consecutive stable steps the chunk skips
+    its remaining blocks.  Every query head of the group follows the chunk's
+    decision.  The output is exact attention over the union of the visited
+    blocks (the per-chunk outputs merge by log-sum-exp, which is order
+    invariant).  patience <= 0 disables the stop.
+
+    Returns the decode_head fields plus ``visited`` [nblk] bool, ``streams``
+    (per chunk: blocks visited, blocks kept, and per step (d_scale, d_dir)).
+    """
+    base = decode_head(q16, pk, V16, L, delta, sm_scale, sink, local, keep=keep)
+    keep = base["keep"]
+    s = base["s_exact"]
+    G = q16.shape[0]
+    nblk = n_blocks(L)
+    Vf = np.asarray(V16, dtype=np.float64)[:L]
+    visited = np.zeros(nblk, dtype=bool)
+    streams = []
+    for blocks in chunk_blocks(nblk, cb, nchunk):
+        kept = [b for b in blocks if keep[b]]
+        m = np.full(G, -np.inf)
+        lsum = np.zeros(G)
+        o = np.zeros((G, HEAD_DIM))
+        prev = None
+        stable = 0
+        steps = []
+        seen = []
+        for b in kept:
+            t = np.arange(b * BLOCK, min(b * BLOCK + BLOCK, L))
+            mb = s[:, t].max(axis=1)
+            mn = np.maximum(m, mb)
+            scale = np.where(np.isfinite(m), np.exp(m - mn), 0.0)
+            w = np.exp(s[:, t] - mn[:, None])
+            o = o * scale[:, None] + w @ Vf[t]
+            lsum = lsum * scale + w.sum(axis=1)
+            m = mn
+            seen.append(b)
+            x = o[0, :ART_PROBE] / lsum[0]
+            if prev is not None:
+                n1, n0 = float(np.linalg.norm(x)), float(np.linalg.norm(prev))
+                d_scale = abs(n1 - n0)
+                d_dir = 1.0 - float(x @ prev) / (n1 * n0) if n1 > 0.0 and n0 > 0.0 else 1.0
+                steps.append((d_scale, d_dir))
+                stable = stable + 1 if (d_scale < tau and d_dir < phi) else 0
+                if patience > 0 and stable >= patience:
+                    break
+            prev = x
+        visited[seen] = True
+        streams.append({"blocks": blocks, "kept": kept, "visited": seen, "steps": steps})
+    tok = np.repeat(visited, BLOCK)[:L]
+    out = attend_tokens(s, V16[:L], np.nonzero(tok)[0])
+    return {**base, "visited": visited, "streams": streams, "out": out}
+
+
 def dense_head(q16: np.ndarray, keys: np.ndarray, V16: np.ndarray, L: int,
                sm_scale: float) -> np.ndarray:
     """Dense decode attention softmax(q k^T * scale) V over tokens [0, L) in fp64."""
