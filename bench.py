@@ -149,9 +149,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     layers = [base] + [base.clone() for _ in range(R - 1)]
     log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
 
-    def step(i, stages=0, select="union"):
+    def step(i, stages=0, select="union", art=None):
         ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
-                        debug={"stages": stages} if stages else None, select=select)
+                        debug={"stages": stages} if stages else None, select=select, art=art)
 
     # eager launches (host-bound for short contexts), for reference
     for i in range(warmup):
@@ -210,11 +210,16 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     }
 
 
+# run-time termination of each chunk's refine stream timed beside the selection
+# variants: (tau, phi, patience)
+ART = (0.05, 0.01, 1)
+
+
 def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, step):
-    """Per-head block sets and per-token masking: time per step, fraction of
-    (query head, token) pairs attended, and the output's deviation from full
-    attention over K-hat (delta = +inf) -- the bytes loaded are the kept
-    blocks' in every variant."""
+    """Per-head block sets, per-token masking and run-time termination: time
+    per step, fraction of (query head, token) pairs attended, and the output's
+    deviation from full attention over K-hat (delta = +inf).  The selection
+    variants load the kept blocks' bytes; termination skips some of them."""
     import sparse_long_context_ffd_amd as ffd
     rows = (w.batch, w.q_heads, 128)
     full = torch.empty(rows, dtype=torch.float16, device="cuda")
@@ -222,18 +227,19 @@ def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, st
     lens = d["seq_lens"].long()
     valid = torch.arange(w.max_len, device="cuda")[None, :] < lens[:, None]          # [B][L_cap]
     res = {}
-    for sel in ("union", "head_block", "head_token"):
+    for sel in ("union", "head_block", "head_token", "art"):
         o = torch.empty(rows, dtype=torch.float16, device="cuda")
         tm = torch.zeros((w.batch, w.q_heads, w.max_len), dtype=torch.uint8, device="cuda")
-        ffd.decode_attn(shape, d["q"], cache, d["seq_lens"], delta, sm_scale, o, ws, debug={"tmask": tm},
-                        select=sel)
+        kw = {"art": ART} if sel == "art" else {"select": sel}
+        ffd.decode_attn(shape, d["q"], cache, d["seq_lens"], delta, sm_scale, o, ws, debug={"tmask": tm}, **kw)
         torch.cuda.synchronize()
         att = ((tm == 1) & valid[:, None, :]).sum().item() / (valid.sum().item() * w.q_heads)
         diff = (o.float() - full.float())
-        g = graph_of([lambda i=i: step(i, select=sel) for i in range(steps)], torch)
+        g = graph_of([lambda i=i: step(i, **kw) for i in range(steps)], torch)
         g.replay()
         us = timed_replay(g, torch) * 1e3 / steps
-        res[sel] = {"us_per_step": round(us, 3), "attended_frac": round(att, 5),
+        res[sel] = {**({"tau_phi_patience": list(ART)} if sel == "art" else {}),
+                    "us_per_step": round(us, 3), "attended_frac": round(att, 5),
                     "max_abs_vs_full": round(diff.abs().max().item(), 6),
                     "rel_l2_vs_full": round((diff.norm() / full.float().norm()).item(), 6)}
         del g

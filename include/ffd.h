@@ -205,6 +205,35 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
                     void* workspace, size_t workspace_bytes, const ffd_debug_t* debug,
                     void* stream);
 
+/* Options of ffd_decode_attn_ex.
+ *  selection     enum ffd_selection
+ *  art_patience  run-time termination of the refine stream (the ART page,
+ *                "Attention Run-time Termination", Method 2.2-2.4), applied
+ *                to every work-group's stream of kept blocks.  The stream
+ *                visits its kept blocks in increasing order (the interleaved
+ *                split of ffd_plan: chunk c holds blocks c, c + n_chunks, ...).
+ *                After each block it takes the probe x = the first 8 channels
+ *                of the running normalised output of the group's first query
+ *                head; from the second block on, a step is stable when
+ *                | ||x|| - ||x_prev|| | < art_tau and 1 - cos(x, x_prev) <
+ *                art_phi, and after art_patience consecutive stable steps the
+ *                stream skips its remaining blocks (all query heads of the
+ *                group follow it).  0 turns it off; > 0 requires
+ *                FFD_SELECT_UNION and finite art_tau, art_phi >= 0.
+ * The debug tmask marks the tokens of the blocks actually refined. */
+typedef struct ffd_decode_opts {
+  int32_t selection;
+  int32_t art_patience;
+  float art_tau;
+  float art_phi;
+} ffd_decode_opts_t;
+
+/* ffd_decode_attn with options (NULL = defaults: union selection, no
+ * run-time termination); invalid options return FFD_ERR_ARG. */
+int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
+                       float delta, float sm_scale, const ffd_decode_opts_t* opts, void* out, void* workspace,
+                       size_t workspace_bytes, const ffd_debug_t* debug, void* stream);
+
 /* ffd_decode_attn with a selection variant (enum ffd_selection; any other
  * value returns FFD_ERR_ARG).  ffd_decode_attn is this call with
  * FFD_SELECT_UNION. */

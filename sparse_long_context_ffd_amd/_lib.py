@@ -21,7 +21,7 @@ STATUS = {
 }
 EXPORTED = (
     "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
-    "ffd_decode_attn", "ffd_decode_attn_select",
+    "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex",
     "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
 )
 
@@ -51,6 +51,11 @@ class Debug(ctypes.Structure):
 SELECTIONS = {"union": 0, "head_block": 1, "head_token": 2}
 
 
+class DecodeOpts(ctypes.Structure):
+    _fields_ = [("selection", ctypes.c_int32), ("art_patience", ctypes.c_int32), ("art_tau", ctypes.c_float),
+                ("art_phi", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -72,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                       P(Debug), V]
         L.ffd_decode_attn_select.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, I32, V,
                                              V, SZ, P(Debug), V]
+        L.ffd_decode_attn_ex.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, P(DecodeOpts),
+                                         V, V, SZ, P(Debug), V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
         L.ffd_strerror.argtypes = [ctypes.c_int]
         L.ffd_strerror.restype = ctypes.c_char_p
@@ -196,9 +203,12 @@ def append_kv(shape: Shape, k_new, v_new, pos, cache: PackedCache, stream=None) 
 
 
 def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,
-                workspace, debug: Optional[dict] = None, stream=None, select: str = "union") -> None:
+                workspace, debug: Optional[dict] = None, stream=None, select: str = "union",
+                art: Optional[Tuple[float, float, int]] = None) -> None:
     """One decode step; ``select`` is "union" (ffd_decode_attn) or a selection
-    variant "head_block" / "head_token" (ffd_decode_attn_select)."""
+    variant "head_block" / "head_token" (ffd_decode_attn_select); ``art`` =
+    (tau, phi, patience) turns on the run-time termination of each chunk's
+    refine stream (ffd_decode_attn_ex)."""
     import torch
     rows = shape.batch * shape.num_q_heads
     _need(q, torch.float16, rows * 128, "q")
@@ -214,7 +224,16 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
         dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
                     debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)),
                     _ptr(debug.get("tmask")))
-    if select == "union":
+    if art is not None:
+        if select not in SELECTIONS:
+            raise ValueError(f"unknown selection {select!r}")
+        opts = DecodeOpts(SELECTIONS[select], int(art[2]), float(art[0]), float(art[1]))
+        _check(lib().ffd_decode_attn_ex(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
+                                        float(delta), float(sm_scale), ctypes.byref(opts), _ptr(out),
+                                        _ptr(workspace), workspace.numel(),
+                                        None if dbg is None else ctypes.byref(dbg), _stream(stream)),
+               "ffd_decode_attn_ex")
+    elif select == "union":
         _check(lib().ffd_decode_attn(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
                                      float(delta), float(sm_scale), _ptr(out), _ptr(workspace),
                                      workspace.numel(), None if dbg is None else ctypes.byref(dbg),

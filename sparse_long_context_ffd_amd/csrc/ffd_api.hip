@@ -88,7 +88,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 extern "C" {
 
-int ffd_version(void) { return 400; }
+int ffd_version(void) { return 500; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -189,6 +189,18 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
 int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
                            const int32_t* seq_lens, float delta, float sm_scale, int32_t selection, void* out,
                            void* workspace, size_t workspace_bytes, const ffd_debug_t* debug, void* stream) {
+  ffd_decode_opts_t o = {};
+  o.selection = selection;
+  return ffd_decode_attn_ex(shape, q, cache, seq_lens, delta, sm_scale, &o, out, workspace, workspace_bytes, debug,
+                            stream);
+}
+
+int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
+                       float delta, float sm_scale, const ffd_decode_opts_t* opts, void* out, void* workspace,
+                       size_t workspace_bytes, const ffd_debug_t* debug, void* stream) {
+  ffd_decode_opts_t o = {};
+  if (opts) o = *opts;
+  const int32_t selection = o.selection;
   const int st = check_shape(shape);
   if (st) return st;
   if (!q || !cache || !seq_lens || !out || !cache->codes || !cache->sz || !cache->res || !cache->rscale ||
@@ -202,6 +214,10 @@ int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_ca
   if (!(sm_scale > 0.f) || isinf(sm_scale)) return FFD_ERR_ARG;
   if (selection != FFD_SELECT_UNION && selection != FFD_SELECT_HEAD_BLOCK && selection != FFD_SELECT_HEAD_TOKEN)
     return FFD_ERR_ARG;
+  if (o.art_patience < 0) return FFD_ERR_ARG;
+  if (o.art_patience > 0 && (selection != FFD_SELECT_UNION || !(o.art_tau >= 0.f) || isinf(o.art_tau) ||
+                             !(o.art_phi >= 0.f) || isinf(o.art_phi)))
+    return FFD_ERR_ARG;
   const Plan pl = make_plan(shape);
   if (!workspace || workspace_bytes < pl.total) return FFD_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FFD_ERR_ALIGN;
@@ -209,6 +225,9 @@ int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_ca
   ffd::DecodeParams p = {};
   p.select = selection;
   p.interleaved = 1;
+  p.art_patience = o.art_patience;
+  p.art_tau = o.art_tau;
+  p.art_phi = o.art_phi;
   char* ws = static_cast<char*>(workspace);
   p.q = static_cast<const uint16_t*>(q);
   p.codes = static_cast<const uint8_t*>(cache->codes);

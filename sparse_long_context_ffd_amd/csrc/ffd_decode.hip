@@ -35,6 +35,7 @@
 namespace ffd {
 
 constexpr int kWaves = 4;
+constexpr int kArtProbe = 8;  // run-time termination probe: first 8 output channels of the group's first head
 // s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited on
 constexpr int kWaitVmcnt0 = 0x0F70;
 
@@ -553,7 +554,7 @@ struct RefineRegs {
 
 // Register budget: 3 waves per SIMD for G <= 4 (<= 168 VGPRs, no spills); the
 // G > 4 variant keeps twice the accumulators and runs at 2.
-template <int G, int SEL>
+template <int G, int SEL, bool ART>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void attend_kernel(
     DecodeParams p) {
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
@@ -606,6 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
   // h) under the per-head block selection
   __shared__ int kflag[kWaves][CBMAX];
+  __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
   float* est = dyn;                                                // [cb][kWaves][G][16]
@@ -809,6 +811,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       }
       st.step(xs, c2, slack, va);
     };
+    // Run-time termination of the chunk's stream (the ART page, Method 2.2-2.4):
+    // after every refined block lane 0 of each wave publishes its running
+    // (max, sum, first kArtProbe output channels) of the group's first head;
+    // after a barrier every thread combines the four wave states into the
+    // chunk's probe x and compares it with the previous one.  All threads
+    // compute the same values from the same LDS words, so the decision is
+    // uniform.  Slots alternate by step parity so that one barrier per step
+    // suffices.
+    int art_step_no = 0, art_stable = 0;
+    float art_prev[kArtProbe];
+    auto art_stop = [&]() -> bool {
+      float* slot = art_lds[art_step_no & 1];
+      if (lane == 0) {
+        slot[wave * (2 + kArtProbe)] = st.m[0];
+        slot[wave * (2 + kArtProbe) + 1] = st.l[0];
+#pragma unroll
+        for (int k = 0; k < kArtProbe; ++k) slot[wave * (2 + kArtProbe) + 2 + k] = st.o[0][k][0];
+      }
+      __syncthreads();
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w)
+        if (slot[w * (2 + kArtProbe) + 1] > 0.f) M = fmaxf(M, slot[w * (2 + kArtProbe)]);
+      float lt = 0.f, x[kArtProbe];
+#pragma unroll
+      for (int k = 0; k < kArtProbe; ++k) x[k] = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* e = slot + w * (2 + kArtProbe);
+        if (e[1] > 0.f) {
+          const float f = __builtin_amdgcn_exp2f((e[0] - M) * c2);
+          lt = fmaf(e[1], f, lt);
+#pragma unroll
+          for (int k = 0; k < kArtProbe; ++k) x[k] = fmaf(e[2 + k], f, x[k]);
+        }
+      }
+      const float inv = 1.f / lt;
+      float n1 = 0.f, n0 = 0.f, dot = 0.f;
+#pragma unroll
+      for (int k = 0; k < kArtProbe; ++k) {
+        x[k] *= inv;
+        n1 = fmaf(x[k], x[k], n1);
+        n0 = fmaf(art_prev[k], art_prev[k], n0);
+        dot = fmaf(x[k], art_prev[k], dot);
+      }
+      bool stop = false;
+      if (art_step_no > 0) {
+        n1 = sqrtf(n1);
+        n0 = sqrtf(n0);
+        const float d_scale = fabsf(n1 - n0);
+        const float d_dir = (n1 > 0.f && n0 > 0.f) ? 1.f - dot / (n1 * n0) : 1.f;
+        art_stable = (d_scale < p.art_tau && d_dir < p.art_phi) ? art_stable + 1 : 0;
+        stop = art_stable >= p.art_patience;
+      }
+#pragma unroll
+      for (int k = 0; k < kArtProbe; ++k) art_prev[k] = x[k];
+      ++art_step_no;
+      return stop;
+    };
     // kept blocks in increasing order from the (wave-uniform) mask; the next
     // one is loaded while the current one is computed, unconditionally as in
     // the scan (the last block is re-read past the end of the mask)
@@ -821,11 +882,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       const int jy = rem ? __builtin_ctzll(rem) : jx;
       load_block(jy, Y);
       refine(jx, X);
+      if constexpr (ART)
+        if (art_stop()) break;
       if (!rem) break;
       rem &= rem - 1;
       const int jn = rem ? __builtin_ctzll(rem) : jy;
       load_block(jn, X);
       refine(jy, Y);
+      if constexpr (ART)
+        if (art_stop()) break;
     }
   }
   st.template store<G>(cl, wave, lane, p.sm_scale);
@@ -983,10 +1048,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int G, int SEL>
+template <int G, int SEL, bool ART>
 static void launch_attend(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attend_kernel<G, SEL>), dim3(p.nchunk, p.Hkv, p.B), dim3(256), AttendCfg<G>::lds_bytes(p.cb),
-                     s, p);
+  hipLaunchKernelGGL((attend_kernel<G, SEL, ART>), dim3(p.nchunk, p.Hkv, p.B), dim3(256),
+                     AttendCfg<G>::lds_bytes(p.cb), s, p);
 }
 template <int G>
 static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
@@ -995,12 +1060,14 @@ static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL(pseudomax_kernel<G>, dim3(p.npart, p.Hkv, p.B), dim3(256), 0, s, p);
   if (stages & 2) {
     if (p.ev_start) (void)hipEventRecord(p.ev_start, s);
-    if (p.select == kSelectHeadBlock)
-      launch_attend<G, kSelectHeadBlock>(p, s);
+    if (p.art_patience > 0)  // run-time termination (union selection only)
+      launch_attend<G, kSelectUnion, true>(p, s);
+    else if (p.select == kSelectHeadBlock)
+      launch_attend<G, kSelectHeadBlock, false>(p, s);
     else if (p.select == kSelectHeadToken)
-      launch_attend<G, kSelectHeadToken>(p, s);
+      launch_attend<G, kSelectHeadToken, false>(p, s);
     else
-      launch_attend<G, kSelectUnion>(p, s);
+      launch_attend<G, kSelectUnion, false>(p, s);
     if (p.ev_stop) (void)hipEventRecord(p.ev_stop, s);
   }
   if (stages & 4) hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);

@@ -32,6 +32,8 @@ struct DecodeParams {
   hipEvent_t ev_stop;
   int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge
   int select;              // kSelectUnion / kSelectHeadBlock / kSelectHeadToken
+  int art_patience;        // run-time termination: stable steps before a chunk stops (0 = off)
+  float art_tau, art_phi;  // ... thresholds on the probe's norm change and 1 - cosine
   int interleaved;         // chunk c holds blocks c + j * nchunk (attend) instead of c * cb + j (dense)
   int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
   float delta, sm_scale;

@@ -68,7 +68,7 @@ def cache_to_host(cache):
     return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
-def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union"):
+def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union", art=None):
     import sparse_long_context_ffd_amd as ffd
     B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
     nb = shape.max_seq_len // 64
@@ -81,7 +81,7 @@ def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, w
         "keep": torch.full((B, Hkv, nb), 7, dtype=torch.uint8, device="cuda"),
         "tmask": torch.full((B, Hq, shape.max_seq_len), 7, dtype=torch.uint8, device="cuda"),
     }
-    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg, select=select)
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg, select=select, art=art)
     torch.cuda.synchronize()
     return {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
 

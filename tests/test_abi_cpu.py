@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 400
+    assert L.ffd_version() == 500
 
 
 def test_strerror_covers_codes():
@@ -107,6 +107,23 @@ def test_decode_select_argument_errors():
         assert _decode_sel(s, sel, q=None) == -1
         assert _decode_sel(s, sel, ws=FAKE + 8) == -3
     assert set(_lib.SELECTIONS.values()) == {0, 1, 2}
+
+
+def _decode_ex(shape, opts, q=FAKE):
+    c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return ffd.lib().ffd_decode_attn_ex(ctypes.byref(shape), q, ctypes.byref(c), FAKE, 5.0, 0.088,
+                                        None if opts is None else ctypes.byref(opts), FAKE, FAKE, _ws(shape),
+                                        None, None)
+
+
+def test_decode_ex_option_errors():
+    s = ffd.make_shape(1, 32, 8, 16384)
+    O = _lib.DecodeOpts
+    for bad in (O(3, 0, 0.0, 0.0), O(0, -1, 0.0, 0.0), O(1, 2, 0.1, 0.1), O(2, 1, 0.1, 0.1),
+                O(0, 1, -0.1, 0.1), O(0, 1, 0.1, math.nan), O(0, 1, math.inf, 0.1), O(0, 1, 0.1, -math.inf)):
+        assert _decode_ex(s, bad) == -6, (bad.selection, bad.art_patience, bad.art_tau, bad.art_phi)
+    for good in (None, O(0, 0, 0.0, 0.0), O(0, 2, 0.05, 0.01), O(2, 0, -1.0, math.nan)):
+        assert _decode_ex(s, good, q=None) == -1       # valid options: the pointer checks still run first
 
 
 def test_dense_and_pack_argument_errors():
