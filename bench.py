@@ -52,8 +52,8 @@ ROTATE_TARGET = 1.5e9
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "cc328da1ecaaa2f5", "fetch": 9917.75, "write": 329.84},
-    "long_256k": {"sources": "cc328da1ecaaa2f5", "fetch": 134979.16, "write": 1437.76},
+    "llama8b_16k": {"sources": "940ed7b8c51c9e70", "fetch": 9932.82, "write": 697.31},
+    "long_256k": {"sources": "940ed7b8c51c9e70", "fetch": 130939.5, "write": 3365.32},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
