@@ -14,7 +14,6 @@ static_assert(ffd::kSelectUnion == FFD_SELECT_UNION && ffd::kSelectHeadBlock == 
                   ffd::kSelectHeadToken == FFD_SELECT_HEAD_TOKEN,
               "selection codes of the ABI and the kernels differ");
 
-
 namespace {
 
 constexpr size_t kAlign = 256;

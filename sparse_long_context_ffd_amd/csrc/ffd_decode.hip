@@ -11,6 +11,11 @@
 //            blocks, exact attention (reusing the stage-2
 //            scores kept on chip)                          -> attend_kernel phase B
 //   log-sum-exp merge of the per-chunk partials            -> merge_kernel
+// Template parameters of attend_kernel: SEL chooses what each query head
+// attends inside the kept blocks (the GQA union, its own kept blocks, or its
+// own tokens by the per-token criterion of Method 2), ART the run-time
+// termination of each chunk's refine stream (the ART page, "Attention Run-time
+// Termination", Method 2.2-2.4).
 //
 // Scores are computed per 16-token tile with MFMA 16x16x32 f16, tokens on the
 // rows.  The B operand holds q with column n = 4*h + g carrying head h
@@ -23,12 +28,13 @@
 //   residual:  A = 1152 + e (exact fp16), accumulator starts at -1152*sum_g(q):
 //              C = q_g . e_g;      exact = est + rscale*C
 //
-// Work decomposition of attend/dense: one work-group (4 wave64) per chunk of `cb`
-// 64-token blocks of one (sequence, KV head) -- contiguous blocks for dense,
-// interleaved over the sequence (stride = number of chunks) for attend.  Wave w owns token tile
-// [16w, 16w+16) of every block of the chunk, so the four waves do identical work
-// and each keeps its own online-softmax state; the states are combined in LDS
-// into one partial per chunk, which merge_kernel combines.
+// Work decomposition of attend/dense: one work-group (4 wave64) per chunk of
+// `cb` 64-token blocks of one (sequence, KV head) -- contiguous blocks for
+// dense, interleaved over the sequence (stride = number of chunks) for attend.
+// Wave w owns token tile [16w, 16w+16) of every block of the chunk, so the
+// four waves do identical work and each keeps its own online-softmax state;
+// the states are combined in LDS into one partial per chunk, which
+// merge_kernel combines.
 #include "ffd_device.h"
 #include "ffd_launch.h"
 
