@@ -111,6 +111,10 @@ struct QFrags {
   static constexpr int NT = (G + 3) / 4;  // 16-column tiles (4 heads x 4 groups each)
   h8 B[NT][kGroups];
   float c_est[NT], c_res[NT], qq[NT];  // accumulator starts; qq = sum_g(q) of the lane's column
+  // transposed scan (estimate_t): Q of head 4*nt + ks for the four groups and
+  // the accumulator start -4*Q of the lane's four C rows
+  float Qt[NT][kGroups];
+  f4 cinit_t[NT];
   uint32_t code_mask, code_one;        // kCodeMask (SGPR), kOneHalf2 (VGPR)
 
   // q of the group's G heads ([G][128] fp16 at `qh`) is read once per
@@ -168,6 +172,34 @@ struct QFrags {
       c_est[nt] = -4.f * Q;
       c_res[nt] = -1152.f * Q;
       qq[nt] = Q;
+      // Q of (head 4*nt + ks, group g) sits in the lanes of column 4*ks + g
+      const int ks = lane >> 4;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) Qt[nt][g] = __shfl(Q, 4 * ks + g, 64);
+      cinit_t[nt] = f4{-4.f * Qt[nt][0], -4.f * Qt[nt][1], -4.f * Qt[nt][2], -4.f * Qt[nt][3]};
+    }
+  }
+
+  // Transposed estimate of the scan: the same registers with the operands
+  // swapped, so the C rows are (head, group) = (4*nt + ks, g) and the columns
+  // are the 16 tokens of the tile; the lane (token col, head row ks) then holds
+  // all four group terms of its (token, head) and sums them without lane
+  // exchanges.  zs = (scale, zero) of the lane's token for groups 0..3.
+  __device__ void estimate_t(uint2 cw, uint4 zs, float (&e)[NT]) const {
+    const h8 a0 = unpack_even(cw.x, code_mask, code_one), a1 = unpack_odd(cw.x, code_mask, code_one);
+    const h8 a2 = unpack_even(cw.y, code_mask, code_one), a3 = unpack_odd(cw.y, code_mask, code_one);
+    const uint32_t z[4] = {zs.x, zs.y, zs.z, zs.w};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f4 c = cinit_t[nt];
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][0], a0, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][1], a1, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][2], a2, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][3], a3, c, 0, 0, 0);
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) acc = fmaf(lo_h(z[g]), c[g], fmaf(hi_h(z[g]), Qt[nt][g], acc));
+      e[nt] = acc;
     }
   }
 
@@ -211,9 +243,10 @@ struct QFrags {
 
 // per-lane byte offsets of one tile's packed data inside a block
 struct TileOffsets {
-  int codes, sz, res, rsc;
+  int codes, sz, szt, res, rsc;
   __device__ TileOffsets(int wave, int lane) {
     const int col = lane & 15, gc = col & 3, ks = lane >> 4;
+    szt = ((ks * 4 + (col >> 2)) * 4 + wave) * 16 + (col & 3) * 4;          // token 16w+col, group ks
     codes = ((col * 4 + ks) * 4 + wave) * 8;                                // A row token 16w+col, slice ks
     sz = ((gc * 4 + ks) * 4 + wave) * 16;                                   // C rows 16w+4ks.., group gc
     res = (((ks >> 1) * 64) + 16 * wave + col) * 16 + 8 * (ks & 1);         // + group * 2048
@@ -586,14 +619,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // while the thumbnail batch is still in flight) ----
   typename QFrags<G>::Stage qst;
   QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
+  // Thumbnail batches: per lane 8 bytes of codes (the token's row of the A
+  // fragments) and one (scale, zero) pair -- token 16w + col, group ks; the
+  // four pairs of a token reach its lanes through ds_bpermute in the scan.
   uint2 cwA[4], cwB[4];
-  uint4 zwA[4], zwB[4];
-  auto load_batch = [&](int j0, uint2 (&cw)[4], uint4 (&zw)[4]) {
+  uint32_t zwA[4], zwB[4];
+  auto load_batch = [&](int j0, uint2 (&cw)[4], uint32_t (&zw)[4]) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int jj = min(j0 + v, nbl_cap - 1);
       cw[v] = buf_load_b64(r_codes, (uint32_t)to.codes, (uint32_t)blk_of(jj) * kCodesBytes);
-      zw[v] = buf_load_b128(r_sz, (uint32_t)to.sz, (uint32_t)blk_of(jj) * kSzBytes);
+      zw[v] = buf_load_b32(r_sz, (uint32_t)to.szt, (uint32_t)blk_of(jj) * kSzBytes);
     }
   };
   load_batch(0, cwA, zwA);
@@ -648,41 +684,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     const int h = 4 * nt + hc;
     thr[nt] = h < G ? (pseudo_max(h) - p.delta) / p.sm_scale : INFINITY;
   }
+  float thr_t[NT];  // threshold of the lane's head in the transposed scan (row group ks)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int h = 4 * nt + ks;
+    thr_t[nt] = h < G ? (pseudo_max(h) - p.delta) / p.sm_scale : INFINITY;
+  }
+  int zsrc[kGroups];  // lanes holding the (scale, zero) pairs of this lane's token, groups 0..3
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) zsrc[g] = (col | (g << 4)) << 2;
   if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
   // sequence end (only in the last block) are set to -inf
-  auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint4 (&zw)[4]) {
+  auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint32_t (&zw)[4]) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = j0 + v;
       if (j < nbl) {
-        float e[NT][4];
-        qf.estimate(cw[v], zw[v], e);
+        const uint4 z4 = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[0], (int)zw[v]),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[1], (int)zw[v]),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[2], (int)zw[v]),
+                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[3], (int)zw[v]));
+        float e[NT];
+        qf.estimate_t(cw[v], z4, e);
         if ((blk_of(j) + 1) * 64 > L) {
-          const int row0 = blk_of(j) * 64 + 16 * wave + 4 * ks;
+          const bool valid = blk_of(j) * 64 + 16 * wave + col < L;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e[nt][i] = (row0 + i < L) ? e[nt][i] : -INFINITY;
+          for (int nt = 0; nt < NT; ++nt) e[nt] = valid ? e[nt] : -INFINITY;
         }
         // per-head block selection: bit h = head h reaches its threshold in
-        // this tile; otherwise one flag for the group
+        // this tile (lanes 16*ks .. 16*ks + 15 hold head 4*nt + ks); otherwise
+        // one flag for the group
         uint32_t hreach = 0;
         bool reach = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float mx = fmaxf(fmaxf(e[nt][0], e[nt][1]), fmaxf(e[nt][2], e[nt][3]));
-          if constexpr (SEL == kSelectHeadBlock)
-            hreach |= head_bits(__builtin_amdgcn_ballot_w64(mx >= thr[nt])) << (4 * nt);
-          else
-            reach = reach || (mx >= thr[nt]);
-          const int h = 4 * nt + hc;
-          if (gc == 0 && h < G) {
-            *reinterpret_cast<float4*>(&est[((j * kWaves + wave) * G + h) * 16 + 4 * ks]) =
-                make_float4(e[nt][0], e[nt][1], e[nt][2], e[nt][3]);
-            if (dbg_bmax) tmax[(j * 4 * kWaves + 4 * wave + ks) * G + h] = mx;
+          if constexpr (SEL == kSelectHeadBlock) {
+            const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
+            hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
+                       (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
+                      << (4 * nt);
+          } else {
+            reach = reach || (e[nt] >= thr_t[nt]);
+          }
+          const int h = 4 * nt + ks;
+          if (h < G) est[((j * kWaves + wave) * G + h) * 16 + col] = e[nt];
+          if (dbg_bmax) {
+            // block-max diagnostic: maximum over each 4-token quad of lanes
+            float qm = fmaxf(e[nt], dpp<kQuadXor1>(e[nt]));
+            qm = fmaxf(qm, dpp<kQuadXor2>(qm));
+            if (h < G && (col & 3) == 0) tmax[(j * 4 * kWaves + 4 * wave + (col >> 2)) * G + h] = qm;
           }
         }
         if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;

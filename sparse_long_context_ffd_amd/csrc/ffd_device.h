@@ -101,6 +101,9 @@ __device__ inline uint2 buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
   return make_uint2(v[0], v[1]);
 }
+__device__ inline uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
 __device__ inline uint4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
