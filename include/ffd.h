@@ -80,15 +80,16 @@ typedef struct ffd_shape {
  * head index b * num_kv_heads + kv_head.  Every field is 16-byte aligned.
  *
  *  codes   uint8  [B][Hkv][nblk][2048]  2-bit codes.  Token t of a block
- *          (tt = t/16, tl = t%16), channel slice kq = 0..3, group pair p = 0..1
- *          own the 32-bit little-endian word at byte
- *              ((tl*4 + kq)*4 + tt)*8 + p*4
+ *          (t = 0..63), channel slice kq = 0..3, group pair p = 0..1 own the
+ *          32-bit little-endian word at byte
+ *              (t*4 + kq)*8 + p*4
  *          holding channels 32g + 8kq + j (j = 0..7) of groups g = 2p and 2p+1:
  *          even g: j = 2d at bit 8+2d,  j = 2d+1 at bit 24+2d   (d = 0..3)
  *          odd g:  j = 2d at bit 2d,    j = 2d+1 at bit 16+2d.
  *  sz      fp16   [B][Hkv][nblk][512]   (scale, zero) pairs.  Token t
  *          (tt = t/16, kq = (t/4)%4, i = t%4), group g: scale at byte
- *              ((g*4 + kq)*4 + tt)*16 + i*4, zero 2 bytes after it.
+ *              ((tt*4 + g)*4 + kq)*16 + i*4, zero 2 bytes after it
+ *          (codes and pairs of the 16-token tile tt are one contiguous run).
  *  res     int8   [B][Hkv][nblk][8192]  residual of token t, channel ch at byte
  *              ((ch/16)*64 + t)*16 + ch%16   (two's complement).
  *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t, group g at

@@ -246,9 +246,9 @@ struct TileOffsets {
   int codes, sz, szt, res, rsc;
   __device__ TileOffsets(int wave, int lane) {
     const int col = lane & 15, gc = col & 3, ks = lane >> 4;
-    szt = ((ks * 4 + (col >> 2)) * 4 + wave) * 16 + (col & 3) * 4;          // token 16w+col, group ks
-    codes = ((col * 4 + ks) * 4 + wave) * 8;                                // A row token 16w+col, slice ks
-    sz = ((gc * 4 + ks) * 4 + wave) * 16;                                   // C rows 16w+4ks.., group gc
+    szt = sz_off(16 * wave + col, ks);                                      // token 16w+col, group ks
+    codes = codes_word_off(16 * wave + col, ks, 0);                         // A row token 16w+col, slice ks
+    sz = sz_off(16 * wave + 4 * ks, gc);                                    // C rows 16w+4ks.., group gc
     res = (((ks >> 1) * 64) + 16 * wave + col) * 16 + 8 * (ks & 1);         // + group * 2048
     rsc = (gc * 64 + 16 * wave + 4 * ks) * 2;                               // C rows, group gc
   }

@@ -11,12 +11,11 @@ def _code_maps():
     word = np.zeros((64, 128), np.int64)
     bit = np.zeros((64, 128), np.int64)
     for t in range(64):
-        tt, tl = divmod(t, 16)
         for ch in range(128):
             g, r = divmod(ch, 32)
             kq, j = divmod(r, 8)
             p = g // 2
-            word[t, ch] = ((tl * 4 + kq) * 4 + tt) * 2 + p          # 32-bit word index in the block
+            word[t, ch] = (t * 4 + kq) * 2 + p                      # 32-bit word index in the block
             d, odd = divmod(j, 2)
             if g % 2 == 0:
                 bit[t, ch] = 24 + 2 * d if odd else 8 + 2 * d
@@ -30,7 +29,7 @@ def _sz_map():
     for t in range(64):
         tt, kq, i = t // 16, (t // 4) % 4, t % 4
         for g in range(4):
-            idx[t, g] = (((g * 4 + kq) * 4 + tt) * 16 + i * 4) // 2   # fp16 element index of the scale
+            idx[t, g] = (((tt * 4 + g) * 4 + kq) * 16 + i * 4) // 2   # fp16 element index of the scale
     return idx
 
 
