@@ -92,8 +92,8 @@ typedef struct ffd_shape {
  *          (codes and pairs of the 16-token tile tt are one contiguous run).
  *  res     int8   [B][Hkv][nblk][8192]  residual of token t, channel ch at byte
  *              ((ch/16)*64 + t)*16 + ch%16   (two's complement).
- *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t, group g at
- *              element g*64 + t.
+ *  rscale  fp16   [B][Hkv][nblk][256]   residual scale of token t (tt = t/16),
+ *              group g at element (tt*4 + g)*16 + t%16.
  *  v       fp16   [B][Hkv][max_seq_len*128]  values, token-quad tiled: token
  *          t, channel ch at element ((t/4)*128 + ch)*4 + t%4 (so the four
  *          tokens 4j..4j+3 of one channel are 8 contiguous bytes; one 64-token

@@ -250,7 +250,7 @@ struct TileOffsets {
     codes = codes_word_off(16 * wave + col, ks, 0);                         // A row token 16w+col, slice ks
     sz = sz_off(16 * wave + 4 * ks, gc);                                    // C rows 16w+4ks.., group gc
     res = (((ks >> 1) * 64) + 16 * wave + col) * 16 + 8 * (ks & 1);         // + group * 2048
-    rsc = (gc * 64 + 16 * wave + 4 * ks) * 2;                               // C rows, group gc
+    rsc = rsc_off(16 * wave + 4 * ks, gc);                                  // C rows 16w+4ks.., group gc
   }
 };
 

@@ -24,16 +24,17 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // packed-cache layout (byte offsets inside one 64-token block of one head).
-// Codes and (scale, zero) are tile-major: the 16 tokens 16w..16w+15 that
-// wave w scans occupy one contiguous 512-byte (codes) and 256-byte
-// (scale, zero) run, so a wave's loads cover whole cache lines.
+// Codes, (scale, zero) and residual scales are tile-major: the 16 tokens
+// 16w..16w+15 that wave w handles occupy one contiguous 512-byte (codes),
+// 256-byte (scale, zero) and 128-byte (residual scale) run, so a wave's loads
+// cover whole cache lines.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int codes_word_off(int t, int kq, int p) { return (t * 4 + kq) * 8 + p * 4; }
 __host__ __device__ inline int sz_off(int t, int g) {
   return (((t >> 4) * 4 + g) * 4 + ((t >> 2) & 3)) * 16 + (t & 3) * 4;
 }
 __host__ __device__ inline int res_off(int t, int ch) { return ((ch >> 4) * 64 + t) * 16 + (ch & 15); }
-__host__ __device__ inline int rsc_off(int t, int g) { return (g * 64 + t) * 2; }
+__host__ __device__ inline int rsc_off(int t, int g) { return (((t >> 4) * 4 + g) * 16 + (t & 15)) * 2; }
 // bit of channel (32g + 8kq + j) inside its word
 __host__ __device__ inline int code_bit(int g, int j) {
   const int d = j >> 1;

@@ -44,7 +44,7 @@ def _res_map():
 _WORD, _BIT = _code_maps()
 _SZ = _sz_map()
 _RES = _res_map()
-_RSC = (np.arange(4)[None, :] * 64 + np.arange(64)[:, None])      # [t][g] -> element g*64 + t
+_RSC = ((np.arange(64)[:, None] // 16) * 4 + np.arange(4)[None, :]) * 16 + np.arange(64)[:, None] % 16  # [t][g]
 
 
 def _v_map(L_cap: int):
