@@ -52,8 +52,8 @@ ROTATE_TARGET = 1.5e9
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "63ef61bb7374d161", "fetch": 9932.82, "write": 697.31},
-    "long_256k": {"sources": "63ef61bb7374d161", "fetch": 130939.5, "write": 3365.32},
+    "llama8b_16k": {"sources": "368228fd6bf56a07", "fetch": 9933.31, "write": 697.31},
+    "long_256k": {"sources": "368228fd6bf56a07", "fetch": 130950.46, "write": 3365.24},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
