@@ -63,7 +63,8 @@ enum ffd_status {
  * at least one support token), max_seq_len a positive multiple of 64,
  * chunk_blocks >= 0 (0 = library choice; otherwise the number of 64-token
  * blocks one work-group scans and refines, capped at 32 for G <= 4 and 16
- * above; it changes only the summation order of the result). */
+ * above; it changes only the summation order of the result), batch and
+ * num_kv_heads at most 65535 (launch-grid dimensions). */
 typedef struct ffd_shape {
   int32_t batch;
   int32_t num_q_heads;

@@ -33,6 +33,8 @@ int check_shape(const ffd_shape_t* s) {
   if (s->sink < 0 || s->local < 0 || s->chunk_blocks < 0) return FFD_ERR_SHAPE;
   if (s->sink == 0 && s->local == 0) return FFD_ERR_SHAPE;  // the pseudo-max needs a support set
   if (s->max_seq_len < 64 || s->max_seq_len % 64 != 0) return FFD_ERR_SHAPE;
+  // batch and KV heads are launch-grid dimensions (at most 65535 each)
+  if (s->batch > 65535 || s->num_kv_heads > 65535) return FFD_ERR_SHAPE;
   return FFD_OK;
 }
 

@@ -678,17 +678,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     for (int pp = 0; pp < n_pt; ++pp) m = fmaxf(m, pm_s[pp * G + h]);
     return m;
   };
-  float thr[NT];  // threshold of the lane column's head, in dot-product units
+  // Pseudo-maxima of the lane's two heads (column head 4*nt + hc for the
+  // refine, row-group head 4*nt + ks for the transposed scan), parts read 8 at
+  // a time so that the LDS reads go out together; part indices are clamped to
+  // the last part (a repeated part leaves a maximum unchanged) and padding
+  // heads h >= G read head G-1 (their thresholds are +inf).
+  float pm_c[NT], pm_k[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int h = 4 * nt + hc;
-    thr[nt] = h < G ? (pseudo_max(h) - p.delta) / p.sm_scale : INFINITY;
+  for (int nt = 0; nt < NT; ++nt) pm_c[nt] = pm_k[nt] = -INFINITY;
+  for (int pp0 = 0; pp0 < n_pt; pp0 += 8) {
+    float vc[NT][8], vk[NT][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = min(pp0 + i, n_pt - 1) * G;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        vc[nt][i] = pm_s[r + min(4 * nt + hc, G - 1)];
+        vk[nt][i] = pm_s[r + min(4 * nt + ks, G - 1)];
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pm_c[nt] = fmaxf(pm_c[nt], vc[nt][i]);
+        pm_k[nt] = fmaxf(pm_k[nt], vk[nt][i]);
+      }
   }
+  float thr[NT];    // threshold of the lane column's head, in dot-product units
   float thr_t[NT];  // threshold of the lane's head in the transposed scan (row group ks)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int h = 4 * nt + ks;
-    thr_t[nt] = h < G ? (pseudo_max(h) - p.delta) / p.sm_scale : INFINITY;
+    thr[nt] = 4 * nt + hc < G ? (pm_c[nt] - p.delta) / p.sm_scale : INFINITY;
+    thr_t[nt] = 4 * nt + ks < G ? (pm_k[nt] - p.delta) / p.sm_scale : INFINITY;
   }
   int zsrc[kGroups];  // lanes holding the (scale, zero) pairs of this lane's token, groups 0..3
 #pragma unroll
@@ -743,17 +765,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       }
     }
   };
-  // Two batches alternate: one is in flight while the other is scanned.  The
-  // loads are unconditional (indices clamped to the chunk, so a batch past the
-  // end re-reads the last block from L2): every path then issues the same
-  // number of loads, which lets the compiler's load counters wait for the
-  // batch being scanned only, not for the one in flight.
-  for (int j0 = 0; j0 < nbl; j0 += 8) {
-    load_batch(j0 + 4, cwB, zwB);
-    scan_batch(j0, cwA, zwA);
-    if (j0 + 4 >= nbl) break;
-    load_batch(j0 + 8, cwA, zwA);
-    scan_batch(j0 + 4, cwB, zwB);
+  // Two batches alternate: one is in flight while the other is scanned.  Inside
+  // the loop every load is unconditional, so the compiler's load counters wait
+  // for the batch being scanned only, not for the one in flight; the last one
+  // or two batches are peeled off, so no load is issued past the chunk (a
+  // load nobody reads would still be waited for when its registers are
+  // reused).  Batch i is in A for even i, in B for odd i.
+  const int nbat = (nbl + 3) >> 2;
+  int i0 = 0;
+  for (; i0 + 2 < nbat; i0 += 2) {
+    load_batch(4 * (i0 + 1), cwB, zwB);
+    scan_batch(4 * i0, cwA, zwA);
+    load_batch(4 * (i0 + 2), cwA, zwA);
+    scan_batch(4 * (i0 + 1), cwB, zwB);
+  }
+  if (i0 + 1 < nbat) {
+    load_batch(4 * (i0 + 1), cwB, zwB);
+    scan_batch(4 * i0, cwA, zwA);
+    scan_batch(4 * (i0 + 1), cwB, zwB);
+  } else {
+    scan_batch(4 * i0, cwA, zwA);
   }
   __syncthreads();
 
@@ -766,8 +797,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     bool kp = false;
     if (lane < nbl) {
       const int blk = blk_of(lane);
-      kp = blk < sink_end || blk >= local_beg || kflag[0][lane] || kflag[1][lane] || kflag[2][lane] ||
-           kflag[3][lane];
+      // the four flags are read unconditionally (one LDS round trip, not a
+      // chain of short-circuit reads)
+      const int any = kflag[0][lane] | kflag[1][lane] | kflag[2][lane] | kflag[3][lane];
+      kp = blk < sink_end || blk >= local_beg || any != 0;
       if (wave == 0) {
         if (p.dbg_keep) p.dbg_keep[head * p.nblk_cap + blk] = kp ? 1 : 0;
         if (dbg_bmax) {

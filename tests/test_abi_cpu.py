@@ -60,6 +60,7 @@ def test_shape_validation():
         dict(head_dim=64), dict(block=32), dict(num_q_heads=30), dict(num_q_heads=72),  # G = 9
         dict(max_seq_len=1000), dict(max_seq_len=0), dict(sink=-1), dict(local=-1),
         dict(sink=0, local=0), dict(chunk_blocks=-2), dict(batch=0), dict(num_kv_heads=0),
+        dict(batch=65536), dict(num_q_heads=65536, num_kv_heads=65536),  # grid dimensions
     ]
     for kw in bad:
         args = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384)
