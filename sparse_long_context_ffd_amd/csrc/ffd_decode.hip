@@ -196,9 +196,13 @@ struct QFrags {
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][1], a1, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][2], a2, c, 0, 0, 0);
       c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][3], a3, c, 0, 0, 0);
+      // zero-point terms first (they do not wait for the MFMA), then the
+      // scale terms
       float acc = 0.f;
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) acc = fmaf(lo_h(z[g]), c[g], fmaf(hi_h(z[g]), Qt[nt][g], acc));
+      for (int g = 0; g < kGroups; ++g) acc = fmaf(hi_h(z[g]), Qt[nt][g], acc);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) acc = fmaf(lo_h(z[g]), c[g], acc);
       e[nt] = acc;
     }
   }
@@ -662,6 +666,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   if (chunk >= nblk) return;
   const int nbl = min(p.cb, (nblk - chunk + nck - 1) / nck);
   const bool dbg_bmax = p.dbg_bmax != nullptr;
+  // Rows past the sequence end get estimate -inf only where it can matter:
+  // with a local window the block holding the last token is always kept (and
+  // the refine masks its rows past the end), so its estimates there decide
+  // nothing; without one, or for the block-max diagnostic, they are masked.
+  const bool tail_mask = p.local == 0 || dbg_bmax;
   // Drain every load issued so far (first batch, q, the pseudo-max parts) so
   // that the pipelined scan below starts from an exact count of loads in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -719,7 +728,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
-  // sequence end (only in the last block) are set to -inf
+  // sequence end (only in the last block) are set to -inf under tail_mask
   auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint32_t (&zw)[4]) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -731,7 +740,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
                                     (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[3], (int)zw[v]));
         float e[NT];
         qf.estimate_t(cw[v], z4, e);
-        if ((blk_of(j) + 1) * 64 > L) {
+        if (tail_mask && (blk_of(j) + 1) * 64 > L) {
           const bool valid = blk_of(j) * 64 + 16 * wave + col < L;
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) e[nt] = valid ? e[nt] : -INFINITY;
