@@ -45,15 +45,15 @@ DENSE_BYTES = 512    # fp16 K + V per token-head
 ROTATE_TARGET = 1.5e9
 # HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
 # `bench.py --workload W --no-long --no-cpu-baseline --steps 20 --warmup 5`
-# (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, mean over the attend
-# dispatches).  Both counters are scaled by what they read for the plain
+# (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the default
+# attend kernel's dispatches).  Both counters are scaled by what they read for the plain
 # 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088 KiB
 # for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "368228fd6bf56a07", "fetch": 9933.31, "write": 697.31},
-    "long_256k": {"sources": "368228fd6bf56a07", "fetch": 130950.46, "write": 3365.24},
+    "llama8b_16k": {"sources": "562604b702a7be39", "fetch": 9916.25, "write": 694.0},
+    "long_256k": {"sources": "562604b702a7be39", "fetch": 134137.38, "write": 3322.5},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
