@@ -61,9 +61,12 @@ def test_decode_qwen_batched_sampled():
     _run(WORKLOADS["qwen7b_b16_16k32k"], 0, [7.0, 3.0], heads=[(0, 0), (5, 3), (15, 1)])
 
 
-@pytest.mark.parametrize("cb", [1, 3, 16])
+@pytest.mark.parametrize("cb", [1, 3, 7, 11, 16, 25, 32])
 def test_decode_chunking_invariance(cb):
-    """The work split changes only the summation order."""
+    """The work split changes only the summation order.  On 64 blocks these
+    chunk sizes give 1, 2, 3, 4, 6 and 8 thumbnail batches of 4 blocks per
+    work-group (each a different path through the scan's loop and its peeled
+    tail), with partial last batches at cb = 3, 7, 11 and 25."""
     _run(WORKLOADS["tiny_h4x1_4k"], 1, [5.0], chunk_blocks=cb)
 
 
