@@ -2,8 +2,9 @@
 """Benchmark one FFD decode-attention step on one MI355X; prints one JSON line.
 
 A step is the whole hot path for one layer: pseudo-max, fused Top-delta scan +
-refine, log-sum-exp merge (three kernel launches), over inputs already resident
-in HBM.  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
+refine, log-sum-exp merge, over inputs already resident in HBM: three kernel
+launches, or two on short caches, where the pseudo-max work-groups lead the
+scan + refine launch (ffd_plan_pseudomax).  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
 delta=5), plus the 256K long-context shape with the in-house dense
 flash-decode kernel timed beside it.
 
@@ -14,12 +15,16 @@ torch.cuda.synchronize().  Per-layer caches are rotated (step i reads copy
 i mod R) so that the bytes touched between two visits of the same copy exceed
 the 256 MB last-level cache.  The fused scan + refine kernel is then timed
 alone: a graph of K back-to-back launches of it (stage mask 2) on the same
-stream; its mean launch duration is the roofline denominator.  Eager
+stream; its mean launch duration is the roofline denominator.  When the
+pseudo-max runs inside that launch it needs the merge of the same step (which
+advances the tag of the published maxima), so its duration is taken as the
+mean of K (scan + refine, merge) launch pairs minus that of K merges alone.  Eager
 (uncaptured) launches are timed too and reported as eager_us_per_step.
 
 Roofline: achieved = algorithmic bytes of the fused kernel per launch (48 B per
-token-head scanned + 392 B per kept token-head refined) / its mean duration,
-against the 8 TB/s HBM3E peak.
+token-head scanned + 392 B per kept token-head refined, + 184 B per support
+token-head when the pseudo-max runs inside it) / its mean duration, against
+the 8 TB/s HBM3E peak.
 """
 from __future__ import annotations
 
@@ -152,6 +157,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     attend_bytes = SCAN_BYTES * tok_total + REFINE_BYTES * kept_tok
     support = sum(min(int(L), w.sink + w.local) for L in lens) * w.kv_heads
     step_bytes = attend_bytes + PSEUDO_BYTES * support
+    _, pm_in_grid = ffd.plan_pseudomax(shape)
+    if pm_in_grid:  # the pseudo-max work-groups are part of the attend launch
+        attend_bytes += PSEUDO_BYTES * support
 
     layer_bytes = sum(n for n in ffd.cache_bytes(shape).values())
     R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
@@ -175,9 +183,14 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     eager_us = t0.elapsed_time(t1) * 1e3 / steps
     # the decode step as the pages run it: captured in a graph (K steps over the
     # rotated layers per replay); W warm-up steps replayed first
-    g_warm, g_steps, g_attend = graph_of([lambda i=i: step(i) for i in range(warmup)], torch), \
-        graph_of([lambda i=i: step(i) for i in range(steps)], torch), \
-        graph_of([lambda i=i: step(i, stages=2) for i in range(steps)], torch)
+    g_warm, g_steps = graph_of([lambda i=i: step(i) for i in range(warmup)], torch), \
+        graph_of([lambda i=i: step(i) for i in range(steps)], torch)
+    if pm_in_grid:
+        g_attend = graph_of([lambda i=i: step(i, stages=6) for i in range(steps)], torch)
+        g_merge = graph_of([lambda i=i: step(i, stages=4) for i in range(steps)], torch)
+    else:
+        g_attend = graph_of([lambda i=i: step(i, stages=2) for i in range(steps)], torch)
+        g_merge = None
     # decode loop: each step first appends one token per sequence (its last one,
     # rewritten with the same key and value, so the cache and the work stay fixed)
     last = d["seq_lens"].long() - 1
@@ -199,6 +212,9 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     wall = time.perf_counter() - wall0
     g_attend.replay()
     attend_total_ms = timed_replay(g_attend, torch)
+    if g_merge is not None:
+        g_merge.replay()
+        attend_total_ms -= timed_replay(g_merge, torch)
     g_loop.replay()
     loop_total_ms = timed_replay(g_loop, torch)
     us_step = total_ms * 1e3 / steps
@@ -210,6 +226,7 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
         "wall_us_per_step": wall * 1e6 / steps,
         "eager_us_per_step": eager_us,
         "attend_us_mean": attend_us,
+        "pm_in_grid": pm_in_grid,
         "loop_us_per_step": loop_total_ms * 1e3 / steps,
         "keep_fraction": keep_frac,
         "attend_bytes": attend_bytes,
@@ -374,7 +391,8 @@ def main():
         "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes(w.name),
-                     "kernel": "attend_kernel (fused Top-delta scan + refine)",
+                     "kernel": "attend_kernel (fused Top-delta scan + refine" +
+                               (", pseudo-max work-groups in the grid)" if r["pm_in_grid"] else ")"),
                      "bytes_per_launch": r["attend_bytes"], "kernel_sources": kernel_digest()},
     }
     del d

@@ -122,7 +122,18 @@ typedef struct ffd_cache {
  *  stages        0 = the whole step; otherwise a bitmask of the launches to
  *                enqueue (1 = pseudo-max, 2 = scan + refine, 4 = merge).  A
  *                partial call reuses what the previous call left in the same
- *                workspace (for timing one kernel alone).                     */
+ *                workspace (for timing one kernel alone).  When the
+ *                pseudo-max runs inside the scan + refine launch (pm_mode),
+ *                bit 1 is ignored.
+ *  pm_mode       where the pseudo-max runs.  0 = the library's choice: inside
+ *                the scan + refine launch for the union selection without
+ *                run-time termination on short caches (chunk work-groups
+ *                <= 1024) when the call enqueues 2 and 4, else its own launch;
+ *                1 = its own launch; 2 = inside the scan + refine launch;
+ *                3 = inside it, but every chunk computes the pseudo-max itself
+ *                (the path of a workspace's first call).  2 and 3 need the
+ *                union selection, no run-time termination and stages 0 or both
+ *                2 and 4, else FFD_ERR_ARG.                                  */
 typedef struct ffd_debug {
   float* m_tilde;
   float* bmax;
@@ -131,6 +142,7 @@ typedef struct ffd_debug {
   void* attend_stop;
   int32_t stages;
   uint8_t* tmask;
+  int32_t pm_mode;
 } ffd_debug_t;
 
 /* What each query head attends inside the blocks kept for its KV head (the
@@ -151,13 +163,25 @@ int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_by
 
 /* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
  * (host call).  The workspace holds partial pseudo-maxima and per-chunk
- * attention partials; its contents need no initialisation.  Calls that share
- * a workspace must be ordered (same stream). */
+ * attention partials; its contents need no initialisation.  It also carries a
+ * step counter from one ffd_decode_attn call to the next: when the pseudo-max
+ * runs inside the scan + refine launch (on short caches, see
+ * ffd_debug_t.pm_mode) its results are tagged with that counter.  The first
+ * such call on a workspace (or the first after a change of batch, query heads
+ * or support size) computes the pseudo-max in every chunk, which is slower;
+ * later calls use the published values.  Calls that share a workspace must be
+ * ordered (same stream). */
 int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
 
 /* Work split chosen for `shape`: blocks per work-group and chunks per
  * sequence (host call). */
 int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks);
+
+/* Where the pseudo-max of a whole ffd_decode_attn step (union selection, no
+ * debug) runs for `shape` (host call): n_parts = support blocks per sequence
+ * (work-groups per KV head), in_grid = 1 when they lead the scan + refine
+ * launch, 0 when they have their own launch (see ffd_debug_t.pm_mode). */
+int ffd_plan_pseudomax(const ffd_shape_t* shape, int32_t* n_parts, int32_t* in_grid);
 
 /* K-cache pack (Method 1): quantize tokens [t_begin, t_end) of every (b, kv
  * head) of `k` (fp16 [B][Hkv][max_seq_len][128]) into `cache` (codes, sz,

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     make_shape,
     pack_v,
     plan,
+    plan_pseudomax,
     quantize_k,
     strerror,
     workspace_bytes,
@@ -24,5 +25,5 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn",
-    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "quantize_k", "strerror", "workspace_bytes",
+    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "workspace_bytes",
 ]

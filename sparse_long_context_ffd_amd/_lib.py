@@ -20,7 +20,7 @@ STATUS = {
     -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP",
 }
 EXPORTED = (
-    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
     "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex",
     "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
 )
@@ -46,7 +46,7 @@ class Cache(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [("m_tilde", ctypes.c_void_p), ("bmax", ctypes.c_void_p), ("keep", ctypes.c_void_p),
                 ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p), ("stages", ctypes.c_int32),
-                ("tmask", ctypes.c_void_p)]
+                ("tmask", ctypes.c_void_p), ("pm_mode", ctypes.c_int32)]
 
 SELECTIONS = {"union": 0, "head_block": 1, "head_token": 2}
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.ffd_cache_bytes.argtypes = [P(Shape), P(SZ), P(SZ), P(SZ), P(SZ), P(SZ)]
         L.ffd_workspace_bytes.argtypes = [P(Shape), P(SZ)]
         L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
+        L.ffd_plan_pseudomax.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_pack_v.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_append_kv.argtypes = [P(Shape), V, V, V, P(Cache), V]
@@ -123,6 +124,14 @@ def plan(shape: Shape) -> Tuple[int, int]:
     cb, nc = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().ffd_plan(ctypes.byref(shape), ctypes.byref(cb), ctypes.byref(nc)), "ffd_plan")
     return cb.value, nc.value
+
+
+def plan_pseudomax(shape: Shape) -> Tuple[int, bool]:
+    """(support parts per sequence, whether a whole union step runs the
+    pseudo-max inside the scan + refine launch)."""
+    n, g = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ffd_plan_pseudomax(ctypes.byref(shape), ctypes.byref(n), ctypes.byref(g)), "ffd_plan_pseudomax")
+    return n.value, bool(g.value)
 
 
 # ---------------------------------------------------------------- tensor plumbing
@@ -223,7 +232,7 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
     if debug is not None:
         dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
                     debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)),
-                    _ptr(debug.get("tmask")))
+                    _ptr(debug.get("tmask")), int(debug.get("pm_mode", 0)))
     if art is not None:
         if select not in SELECTIONS:
             raise ValueError(f"unknown selection {select!r}")

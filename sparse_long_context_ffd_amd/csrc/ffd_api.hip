@@ -17,6 +17,7 @@ static_assert(ffd::kSelectUnion == FFD_SELECT_UNION && ffd::kSelectHeadBlock == 
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr long long kPmgMaxGroups = 1024;  // chunk work-groups up to which the pseudo-max runs in the grid
 constexpr int kTargetGroups = 2048;  // work-groups per launch the automatic split aims for
 constexpr int kSmallGroups = 256;    // ... and at least this many blocks per 4-block group on short caches
 
@@ -40,7 +41,7 @@ int check_shape(const ffd_shape_t* s) {
 
 struct Plan {
   int nblk_cap, cb, nchunk, npart;
-  size_t pmax_off, ml_off, o_off, total;
+  size_t sync_off, pmw_off, pmax_off, ml_off, o_off, total;
 };
 
 // Work split: one work-group per chunk of cb blocks (4 waves, one 16-token tile
@@ -76,8 +77,12 @@ Plan make_plan(const ffd_shape_t* s) {
   const long long np = sink_blocks + local_blocks;
   p.npart = (int)(np < p.nblk_cap ? np : p.nblk_cap);
   const size_t rows = (size_t)s->batch * s->num_q_heads;
-  p.pmax_off = 0;
-  p.ml_off = round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(float), kAlign);
+  // the in-grid pseudo-max's sync words sit at the start for every shape, so
+  // the epoch they hold carries over when a workspace changes shape
+  p.sync_off = 0;
+  p.pmw_off = kAlign;
+  p.pmax_off = p.pmw_off + round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(uint64_t), kAlign);
+  p.ml_off = p.pmax_off + round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(float), kAlign);
   p.o_off = p.ml_off + round_up(rows * p.nchunk * 2 * sizeof(float), kAlign);
   p.total = p.o_off + round_up(rows * p.nchunk * 128 * sizeof(float), kAlign);
   return p;
@@ -85,11 +90,19 @@ Plan make_plan(const ffd_shape_t* s) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
+// default placement of the pseudo-max for a whole union step: inside the
+// attend launch when its words fit one per thread of a work-group and the
+// chunks fit about one round of work-groups on the device (short caches)
+bool pm_default_in_grid(const ffd_shape_t* s, const Plan& pl) {
+  const bool fits = (long long)pl.npart * (s->num_q_heads / s->num_kv_heads) <= 256;
+  return fits && (long long)pl.nchunk * s->num_kv_heads * s->batch <= kPmgMaxGroups;
+}
+
 }  // namespace
 
 extern "C" {
 
-int ffd_version(void) { return 500; }
+int ffd_version(void) { return 600; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -134,6 +147,16 @@ int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks)
   const Plan p = make_plan(shape);
   *chunk_blocks = p.cb;
   *n_chunks = p.nchunk;
+  return FFD_OK;
+}
+
+int ffd_plan_pseudomax(const ffd_shape_t* shape, int32_t* n_parts, int32_t* in_grid) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!n_parts || !in_grid) return FFD_ERR_NULL;
+  const Plan p = make_plan(shape);
+  *n_parts = p.npart;
+  *in_grid = pm_default_in_grid(shape, p) ? 1 : 0;
   return FFD_OK;
 }
 
@@ -240,8 +263,13 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
   p.pmax = reinterpret_cast<float*>(ws + pl.pmax_off);
   p.part_ml = reinterpret_cast<float2*>(ws + pl.ml_off);
   p.part_o = reinterpret_cast<float*>(ws + pl.o_off);
+  p.pm_words = reinterpret_cast<unsigned long long*>(ws + pl.pmw_off);
+  p.pm_sync = reinterpret_cast<unsigned long long*>(ws + pl.sync_off);
+  int pm_mode = 0;
   if (debug) {
     if (debug->stages < 0 || debug->stages > 7) return FFD_ERR_ARG;
+    if (debug->pm_mode < 0 || debug->pm_mode > 3) return FFD_ERR_ARG;
+    pm_mode = debug->pm_mode;
     p.stages = debug->stages;
     p.dbg_mt = debug->m_tilde;
     p.dbg_bmax = debug->bmax;
@@ -263,6 +291,23 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
   p.local = shape->local;
   p.delta = delta;
   p.sm_scale = sm_scale;
+  // Pseudo-max inside the attend launch: possible for the union selection
+  // without run-time termination, when the call also enqueues the merge (which
+  // advances the epoch of the published words) and the words fit one per
+  // thread of a work-group.  Chosen by default only when the chunks fit about
+  // one round of work-groups on the device (short caches): there the separate
+  // launch's latency is on the critical path, while on long caches the chunks
+  // that start with the pseudo-max work-groups would wait for them.  The
+  // magic the merge writes is keyed to the word layout, so words left by
+  // another shape are never trusted.
+  const bool whole = p.stages == 0 || (p.stages & 6) == 6;
+  const bool fits = (long long)pl.npart * (shape->num_q_heads / shape->num_kv_heads) <= 256;
+  const bool can = selection == FFD_SELECT_UNION && o.art_patience == 0 && whole && fits;
+  if (pm_mode >= 2 && !can) return FFD_ERR_ARG;
+  p.pm_in_grid = pm_mode >= 2 || (pm_mode == 0 && can && pm_default_in_grid(shape, pl));
+  p.pm_local = pm_mode == 3;
+  p.pm_magic = ffd::kPmMagic ^ ((unsigned long long)shape->batch << 40) ^ ((unsigned long long)shape->num_q_heads << 24) ^
+               ((unsigned long long)pl.npart << 4);
   return from_hip(ffd::launch_ffd_decode(p, static_cast<hipStream_t>(stream)));
 }
 

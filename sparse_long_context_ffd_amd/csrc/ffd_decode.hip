@@ -267,12 +267,86 @@ __device__ inline void load_residual(const int8_t* rb, const uint8_t* sb, const 
 
 // ---------------------------------------------------------------------------
 // Stage 1: pseudo-max over support tokens [0, min(S,L)) U [max(0,L-W), L),
-// exact scores with K-hat.  Grid (npart, Hkv, B), 4 waves: work-group `part`
-// takes one block holding support tokens (sink blocks first, then local
-// blocks not already covered), wave w its 16-token tile.  Writes the part's
+// exact scores with K-hat.  The support parts of a head are the blocks that
+// can hold support tokens: the sink blocks first, then the local-window blocks
+// not already covered.  Wave w of a work-group takes its 16-token tile of a
+// part; the part's maximum per query head goes to the attend kernel either
+// through a separate launch (pseudomax_kernel) or through 64-bit words written
+// by the leading work-groups of the attend launch itself.
+// ---------------------------------------------------------------------------
+struct SupportTile {
+  uint2 cw;
+  uint4 zw;
+  uint2 R[kGroups], S8;
+  int blk;    // block index (0 when the part is past the sequence)
+  bool live;  // the part is a block of the sequence
+};
+
+// issue the loads of the wave's tile of support part `part` (head = b*Hkv + kv head)
+__device__ inline void support_tile_load(const DecodeParams& p, int part, size_t head, int L, int wave, int lane,
+                                         SupportTile& st) {
+  const int nblk = (L + 63) >> 6;
+  const int s_end = min(p.sink, L);
+  const int l_beg = p.local > 0 ? max(0, L - p.local) : L;
+  const int n_sink_blk = (s_end + 63) >> 6;
+  const int first_local = max(l_beg >> 6, n_sink_blk);
+  const int blk = part < n_sink_blk ? part : first_local + (part - n_sink_blk);
+  st.live = blk < nblk && (part < n_sink_blk || l_beg < L);
+  st.blk = st.live ? blk : 0;
+  const size_t bi = head * p.nblk_cap + st.blk;
+  const TileOffsets to(wave, lane);
+  st.cw = *reinterpret_cast<const uint2*>(p.codes + bi * kCodesBytes + to.codes);
+  st.zw = *reinterpret_cast<const uint4*>(p.sz + bi * kSzBytes + to.sz);
+  load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, st.R, st.S8);
+}
+
+// largest exact score (softmax logit) over the support tokens of the tile, per
+// lane for head 4*nt + hc (reduced over the tile's rows; -inf without support)
+template <int G>
+__device__ void support_tile_max(const DecodeParams& p, const QFrags<G>& qf, const SupportTile& st, int L,
+                                 int wave, int lane, float (&mx)[QFrags<G>::NT]) {
+  constexpr int NT = QFrags<G>::NT;
+  const int s_end = min(p.sink, L);
+  const int l_beg = p.local > 0 ? max(0, L - p.local) : L;
+  float e[NT][4], r[NT][4];
+  qf.estimate(st.cw, st.zw, e);
+  qf.residual(st.R, st.S8, r);
+  const int ks = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = st.blk * 64 + 16 * wave + 4 * ks + i;
+      const bool sup = st.live && t < L && (t < s_end || t >= l_beg);
+      m = fmaxf(m, sup ? (e[nt][i] + r[nt][i]) * p.sm_scale : -INFINITY);
+    }
+    mx[nt] = rows_max(m);
+  }
+}
+
+// the work-group's maximum per query head h < G (valid in threads tid < G)
+// from the per-lane tile maxima; `red` is [kWaves][G] in LDS
+template <int G>
+__device__ float support_wg_max(const float (&mx)[QFrags<G>::NT], float (&red)[kWaves][G], int tid) {
+  constexpr int NT = QFrags<G>::NT;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int h = 4 * nt + hc;
+    if (ks == 0 && gc == 0 && h < G) red[wave][h] = mx[nt];
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  if (tid < G) m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+  __syncthreads();
+  return m;
+}
+
+// Separate launch: grid (npart, Hkv, B), work-group `part` writes its part's
 // maximum per query head (-inf for parts without a block); the attend kernel
 // takes the maximum over parts.
-// ---------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   constexpr int NT = QFrags<G>::NT;
@@ -285,48 +359,18 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   typename QFrags<G>::Stage qst;
   QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
   const int L = clamp_len(p, b);
-  const int nblk = (L + 63) >> 6;
-  const int s_end = min(p.sink, L);
-  const int l_beg = p.local > 0 ? max(0, L - p.local) : L;
-  const int n_sink_blk = (s_end + 63) >> 6;
-  const int first_local = max(l_beg >> 6, n_sink_blk);
-  const int blk = part < n_sink_blk ? part : first_local + (part - n_sink_blk);
-  const bool live = blk < nblk && (part < n_sink_blk || l_beg < L);
-  const int blk_c = live ? blk : 0;
-  const size_t bi = head * p.nblk_cap + blk_c;
-  const TileOffsets to(wave, lane);
-  const uint2 cw = *reinterpret_cast<const uint2*>(p.codes + bi * kCodesBytes + to.codes);
-  const uint4 zw = *reinterpret_cast<const uint4*>(p.sz + bi * kSzBytes + to.sz);
-  uint2 R[kGroups], S8;
-  load_residual(p.res + bi * kResBytes, p.rsc + bi * kRscBytes, to, R, S8);
+  SupportTile st;
+  support_tile_load(p, part, head, L, wave, lane, st);
   QFrags<G>::stage_store(qst, tid, qs);
   __syncthreads();
   typename QFrags<G>::Load ql;
   QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
   qf.build(ql, lane);
-  float e[NT][4], r[NT][4];
-  qf.estimate(cw, zw, e);
-  qf.residual(R, S8, r);
-  const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = blk_c * 64 + 16 * wave + 4 * ks + i;
-      const bool sup = live && t < L && (t < s_end || t >= l_beg);
-      mx = fmaxf(mx, sup ? (e[nt][i] + r[nt][i]) * p.sm_scale : -INFINITY);
-    }
-    mx = rows_max(mx);
-    const int h = 4 * nt + hc;
-    if (ks == 0 && gc == 0 && h < G) red[wave][h] = mx;
-  }
-  __syncthreads();
-  if (tid < G) {
-    const float m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-    p.pmax[((size_t)b * p.npart + part) * p.Hq + qh0 + tid] = m;
-  }
+  float mx[NT];
+  support_tile_max<G>(p, qf, st, L, wave, lane, mx);
+  const float m = support_wg_max<G>(mx, red, tid);
+  if (tid < G) p.pmax[((size_t)b * p.npart + part) * p.Hq + qh0 + tid] = m;
 }
 
 // ---------------------------------------------------------------------------
@@ -580,6 +624,37 @@ struct MfmaSoftmax {
 // group) maxima [cb][16][G] (written only for the block-max diagnostic), the
 // combine area.
 // ---------------------------------------------------------------------------
+// One leading work-group of the attend grid: support part `part` of (b, hkv),
+// published as the 64-bit word (epoch + 1) << 32 | fp32 bits per query head
+// with agent-scope stores (the chunk work-groups read them with agent-scope
+// loads, so no cache maintenance is needed).  `red` is LDS scratch.
+template <int G>
+__device__ void pm_group(const DecodeParams& p, int part, int hkv, int b, uint32_t* qs, float (&red)[kWaves][G]) {
+  constexpr int NT = QFrags<G>::NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t head = (size_t)b * p.Hkv + hkv;
+  const int qh0 = hkv * G;
+  typename QFrags<G>::Stage qst;
+  QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
+  const unsigned long long ep = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int L = clamp_len(p, b);
+  SupportTile st;
+  support_tile_load(p, part, head, L, wave, lane, st);
+  QFrags<G>::stage_store(qst, tid, qs);
+  __syncthreads();
+  typename QFrags<G>::Load ql;
+  QFrags<G>::load(qs, lane, ql);
+  QFrags<G> qf;
+  qf.build(ql, lane);
+  float mx[NT];
+  support_tile_max<G>(p, qf, st, L, wave, lane, mx);
+  const float m = support_wg_max<G>(mx, red, tid);
+  if (tid < G)
+    __hip_atomic_store(p.pm_words + ((size_t)b * p.npart + part) * p.Hq + qh0 + tid,
+                       ((unsigned long long)((uint32_t)ep + 1u) << 32) | __builtin_bit_cast(uint32_t, m),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int G>
 struct AttendCfg {
   static constexpr int NT = QFrags<G>::NT;
@@ -597,13 +672,29 @@ struct RefineRegs {
 
 // Register budget: 3 waves per SIMD for G <= 4 (<= 168 VGPRs, no spills); the
 // G > 4 variant keeps twice the accumulators and runs at 2.
-template <int G, int SEL, bool ART>
+// PMG: the pseudo-max work-groups lead the grid; the chunks then scan before
+// they know their thresholds and take the block decisions from the stored
+// estimates after the scan (so that the wait for the published words overlaps
+// the scan).  Without PMG the thresholds come from the separate launch's
+// partial maxima before the scan, which takes the decisions as it goes.
+template <int G, int SEL, bool ART, bool PMG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void attend_kernel(
     DecodeParams p) {
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
-  const int chunk = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int hkv = blockIdx.y, b = blockIdx.z;
+  __shared__ uint32_t qs[G * 64];
+  __shared__ float pm_s[256];
+  __shared__ float pm_red[kWaves][G];
+  // with the pseudo-max in the grid, the first npart work-groups of each row
+  // compute its support parts (dispatched ahead of the row's chunks)
+  const int npg = PMG ? p.npart : 0;
+  if (PMG && (int)blockIdx.x < npg) {
+    pm_group<G>(p, blockIdx.x, hkv, b, qs, pm_red);
+    return;
+  }
+  const int chunk = (int)blockIdx.x - npg;
   // the chunk's blocks are interleaved over the sequence: block j of chunk c
   // is c + j * nchunk, so the always-kept sink and local-window blocks (and
   // any cluster of kept blocks) spread over many work-groups
@@ -641,14 +732,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // thread (maximum over several parts when there are more than 256/G)
   const int n_pm = p.npart * G;
   float pm_t = -INFINITY;
-  {
+  unsigned long long pw = 0, pm_magic = 0, pm_epoch = 0;  // in-grid word of (part tid/G, head tid%G), sync
+  unsigned long long* const pm_word = p.pm_words + ((size_t)b * p.npart + tid / G) * p.Hq + qh0 + tid % G;
+  if constexpr (PMG) {  // (the host keeps npart * G <= 256 here: one word per thread)
+    if (tid < n_pm) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pm_magic = __hip_atomic_load(p.pm_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pm_epoch = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
     const float* pm = p.pmax + (size_t)b * p.npart * p.Hq + qh0;
     if (tid < n_pm) pm_t = pm[(size_t)(tid / G) * p.Hq + tid % G];
     for (int i = tid + (256 / G) * G; i < n_pm; i += (256 / G) * G) pm_t = fmaxf(pm_t, pm[(size_t)(i / G) * p.Hq + i % G]);
   }
 
-  __shared__ uint32_t qs[G * 64];
-  __shared__ float pm_s[256];
   QFrags<G>::stage_store(qst, tid, qs);
   // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
   // h) under the per-head block selection
@@ -674,57 +769,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // Drain every load issued so far (first batch, q, the pseudo-max parts) so
   // that the pipelined scan below starts from an exact count of loads in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  pm_s[tid] = pm_t;
-  __syncthreads();
+  if constexpr (!PMG) pm_s[tid] = pm_t;
+  __syncthreads();  // q staged in LDS (and the partial maxima without PMG)
   typename QFrags<G>::Load ql;
   QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
   qf.build(ql, lane);
+  int zsrc[kGroups];  // lanes holding the (scale, zero) pairs of this lane's token, groups 0..3
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) zsrc[g] = (col | (g << 4)) << 2;
   // pseudo-max of head h: maximum over the parts of the per-thread values
-  const int n_pt = min(n_pm, (256 / G) * G) / G;  // parts held in pm_s
+  int n_pt = min(n_pm, (256 / G) * G) / G;  // parts held in pm_s
+  float thr[NT];    // threshold of the lane column's head, in dot-product units
+  float thr_t[NT];  // threshold of the lane's head in the transposed scan (row group ks)
   auto pseudo_max = [&](int h) {
     float m = -INFINITY;
     for (int pp = 0; pp < n_pt; ++pp) m = fmaxf(m, pm_s[pp * G + h]);
     return m;
   };
-  // Pseudo-maxima of the lane's two heads (column head 4*nt + hc for the
-  // refine, row-group head 4*nt + ks for the transposed scan), parts read 8 at
-  // a time so that the LDS reads go out together; part indices are clamped to
-  // the last part (a repeated part leaves a maximum unchanged) and padding
-  // heads h >= G read head G-1 (their thresholds are +inf).
-  float pm_c[NT], pm_k[NT];
+  auto compute_thresholds = [&]() {
+    // Pseudo-maxima of the lane's two heads (column head 4*nt + hc for the
+    // refine, row-group head 4*nt + ks for the transposed scan), parts read 8 at
+    // a time so that the LDS reads go out together; part indices are clamped to
+    // the last part (a repeated part leaves a maximum unchanged) and padding
+    // heads h >= G read head G-1 (their thresholds are +inf).
+    float pm_c[NT], pm_k[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) pm_c[nt] = pm_k[nt] = -INFINITY;
-  for (int pp0 = 0; pp0 < n_pt; pp0 += 8) {
-    float vc[NT][8], vk[NT][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = min(pp0 + i, n_pt - 1) * G;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        vc[nt][i] = pm_s[r + min(4 * nt + hc, G - 1)];
-        vk[nt][i] = pm_s[r + min(4 * nt + ks, G - 1)];
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NT; ++nt) pm_c[nt] = pm_k[nt] = -INFINITY;
+    for (int pp0 = 0; pp0 < n_pt; pp0 += 8) {
+      float vc[NT][8], vk[NT][8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        pm_c[nt] = fmaxf(pm_c[nt], vc[nt][i]);
-        pm_k[nt] = fmaxf(pm_k[nt], vk[nt][i]);
+        const int r = min(pp0 + i, n_pt - 1) * G;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          vc[nt][i] = pm_s[r + min(4 * nt + hc, G - 1)];
+          vk[nt][i] = pm_s[r + min(4 * nt + ks, G - 1)];
+        }
       }
-  }
-  float thr[NT];    // threshold of the lane column's head, in dot-product units
-  float thr_t[NT];  // threshold of the lane's head in the transposed scan (row group ks)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    thr[nt] = 4 * nt + hc < G ? (pm_c[nt] - p.delta) / p.sm_scale : INFINITY;
-    thr_t[nt] = 4 * nt + ks < G ? (pm_k[nt] - p.delta) / p.sm_scale : INFINITY;
-  }
-  int zsrc[kGroups];  // lanes holding the (scale, zero) pairs of this lane's token, groups 0..3
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) zsrc[g] = (col | (g << 4)) << 2;
-  if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
+        for (int i = 0; i < 8; ++i) {
+          pm_c[nt] = fmaxf(pm_c[nt], vc[nt][i]);
+          pm_k[nt] = fmaxf(pm_k[nt], vk[nt][i]);
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      thr[nt] = 4 * nt + hc < G ? (pm_c[nt] - p.delta) / p.sm_scale : INFINITY;
+      thr_t[nt] = 4 * nt + ks < G ? (pm_k[nt] - p.delta) / p.sm_scale : INFINITY;
+    }
+    if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
+  };
+  if constexpr (!PMG) compute_thresholds();
+  // In-grid pseudo-max: every word must carry this step's tag (epoch + 1).
+  // The words loaded in the prologue are usually not there yet (their
+  // work-groups started with this one), so the words still missing are loaded
+  // again before the scan and checked after it, where the thresholds are
+  // first needed; words still missing then are polled a bounded number of
+  // times, after which (or before the merge has initialised the sync words, or
+  // under pm_local) the work-group computes the pseudo-max itself.  All
+  // conditions are work-group uniform.
+  const uint32_t pm_want = (uint32_t)pm_epoch + 1u;
+  const bool pm_trusted = PMG && pm_magic == p.pm_magic && !p.pm_local;
+  bool pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+  if (pm_trusted && !pm_mine) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
@@ -747,18 +857,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         }
         // per-head block selection: bit h = head h reaches its threshold in
         // this tile (lanes 16*ks .. 16*ks + 15 hold head 4*nt + ks); otherwise
-        // one flag for the group
+        // one flag for the group (without PMG; with it after the scan)
         uint32_t hreach = 0;
         bool reach = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if constexpr (SEL == kSelectHeadBlock) {
-            const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
-            hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
-                       (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
-                      << (4 * nt);
-          } else {
-            reach = reach || (e[nt] >= thr_t[nt]);
+          if constexpr (!PMG) {
+            if constexpr (SEL == kSelectHeadBlock) {
+              const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
+              hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
+                         (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
+                        << (4 * nt);
+            } else {
+              reach = reach || (e[nt] >= thr_t[nt]);
+            }
           }
           const int h = 4 * nt + ks;
           if (h < G) est[((j * kWaves + wave) * G + h) * 16 + col] = e[nt];
@@ -769,8 +881,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
             if (h < G && (col & 3) == 0) tmax[(j * 4 * kWaves + 4 * wave + (col >> 2)) * G + h] = qm;
           }
         }
-        if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
-        if (lane == 0) kflag[wave][j] = (int)hreach;
+        if constexpr (!PMG) {
+          if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
+          if (lane == 0) kflag[wave][j] = (int)hreach;
+        }
       }
     }
   };
@@ -794,6 +908,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     scan_batch(4 * (i0 + 1), cwB, zwB);
   } else {
     scan_batch(4 * i0, cwA, zwA);
+  }
+
+  // ---- PMG: pseudo-maxima, thresholds and the reach flags after the scan ----
+  if constexpr (PMG) {
+    bool pm_fb = false;
+    {
+      pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+      int all = __syncthreads_and(pm_trusted && pm_mine);
+      for (int s = 0; !all && pm_trusted && s < kPmSpin; ++s) {
+        __builtin_amdgcn_s_sleep(8);
+        if (!pm_mine) {
+          pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          pm_mine = (uint32_t)(pw >> 32) == pm_want;
+        }
+        all = __syncthreads_and(pm_mine);
+      }
+      pm_fb = !all;
+      pm_t = (tid < n_pm && !pm_fb) ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
+    }
+    pm_s[tid] = pm_t;
+    __syncthreads();
+    if (pm_fb) {
+      float m = -INFINITY;  // (threads tid < G) head tid
+      for (int part = 0; part < p.npart; ++part) {
+        SupportTile st;
+        support_tile_load(p, part, head, L, wave, lane, st);
+        float mx[NT];
+        support_tile_max<G>(p, qf, st, L, wave, lane, mx);
+        m = fmaxf(m, support_wg_max<G>(mx, pm_red, tid));
+      }
+      if (tid < G) pm_s[tid] = m;
+      __syncthreads();
+      n_pt = 1;
+    }
+    compute_thresholds();
+
+    // ---- reach flags from the stored estimates, now that the thresholds are
+    // known: per head, or one flag for the group (lanes 16*ks .. 16*ks + 15
+    // hold head 4*nt + ks; each lane reads back the estimates it stored).  The
+    // reads go out 8 blocks at a time (indices clamped to the chunk).
+    for (int j0 = 0; j0 < nbl; j0 += 8) {
+      float e8[8][NT];
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int j = min(j0 + v, nbl - 1);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int h = 4 * nt + ks;
+          e8[v][nt] = h < G ? est[((j * kWaves + wave) * G + h) * 16 + col] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        if (j0 + v < nbl) {
+          uint32_t hreach = 0;
+          bool reach = false;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            if constexpr (SEL == kSelectHeadBlock) {
+              const uint64_t bal = __builtin_amdgcn_ballot_w64(e8[v][nt] >= thr_t[nt]);
+              hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
+                         (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
+                        << (4 * nt);
+            } else {
+              reach = reach || (e8[v][nt] >= thr_t[nt]);
+            }
+          }
+          if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
+          if (lane == 0) kflag[wave][j0 + v] = (int)hreach;
+        }
+      }
+    }
   }
   __syncthreads();
 
@@ -1095,6 +1281,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int h = blockIdx.x, b = blockIdx.y, slice = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int cp = tid >> 5, ch = 32 * slice + (tid & 31);
+  // the step's in-grid pseudo-max words are consumed: advance the epoch (the
+  // next attend launch sees it) and mark the sync words initialised
+  if (p.pm_in_grid && h == 0 && b == 0 && slice == 0 && tid == 0) {
+    const unsigned long long e = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.pm_sync + 1, (unsigned long long)((uint32_t)e + 1u), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.pm_sync, p.pm_magic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   const size_t row = (size_t)b * p.Hq + h;
   const float2* ml = p.part_ml + row * p.nchunk;
   const float* po = p.part_o + row * p.nchunk * kHeadDim + ch;
@@ -1149,26 +1343,28 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int G, int SEL, bool ART>
+template <int G, int SEL, bool ART, bool PMG>
 static void launch_attend(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attend_kernel<G, SEL, ART>), dim3(p.nchunk, p.Hkv, p.B), dim3(256),
+  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), dim3(p.nchunk + (PMG ? p.npart : 0), p.Hkv, p.B), dim3(256),
                      AttendCfg<G>::lds_bytes(p.cb), s, p);
 }
 template <int G>
 static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
   const int stages = p.stages ? p.stages : 7;
-  if (stages & 1)
+  if ((stages & 1) && !p.pm_in_grid)
     hipLaunchKernelGGL(pseudomax_kernel<G>, dim3(p.npart, p.Hkv, p.B), dim3(256), 0, s, p);
   if (stages & 2) {
     if (p.ev_start) (void)hipEventRecord(p.ev_start, s);
-    if (p.art_patience > 0)  // run-time termination (union selection only)
-      launch_attend<G, kSelectUnion, true>(p, s);
+    if (p.pm_in_grid)  // (union selection without run-time termination only)
+      launch_attend<G, kSelectUnion, false, true>(p, s);
+    else if (p.art_patience > 0)  // run-time termination (union selection only)
+      launch_attend<G, kSelectUnion, true, false>(p, s);
     else if (p.select == kSelectHeadBlock)
-      launch_attend<G, kSelectHeadBlock, false>(p, s);
+      launch_attend<G, kSelectHeadBlock, false, false>(p, s);
     else if (p.select == kSelectHeadToken)
-      launch_attend<G, kSelectHeadToken, false>(p, s);
+      launch_attend<G, kSelectHeadToken, false, false>(p, s);
     else
-      launch_attend<G, kSelectUnion, false>(p, s);
+      launch_attend<G, kSelectUnion, false, false>(p, s);
     if (p.ev_stop) (void)hipEventRecord(p.ev_stop, s);
   }
   if (stages & 4) hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);

@@ -11,6 +11,12 @@ constexpr int kSelectUnion = 0;      // every valid token
 constexpr int kSelectHeadBlock = 1;  // forced blocks and blocks reaching the head's own threshold
 constexpr int kSelectHeadToken = 2;  // support tokens and tokens reaching the head's own threshold
 
+// in-grid pseudo-max: the workspace's sync words are trusted once the merge
+// has written this value; polls of a part's word before a chunk computes the
+// pseudo-max itself (each poll sleeps ~512 clocks plus a memory round trip)
+constexpr unsigned long long kPmMagic = 0x4646442d706d6178ull;
+constexpr int kPmSpin = 4096;
+
 struct DecodeParams {
   const uint16_t* q;       // [B][Hq][128] fp16
   const uint8_t* codes;    // packed cache fields (layouts in include/ffd.h)
@@ -20,7 +26,12 @@ struct DecodeParams {
   const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
   const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]: token-quad tiled (FFD), natural (dense)
   const int32_t* seq_lens; // [B]
-  float* pmax;             // [B][npart][Hq] partial pseudo-maxima
+  float* pmax;             // [B][npart][Hq] partial pseudo-maxima (separate pseudo-max launch)
+  // Pseudo-max inside the attend launch: the first npart work-groups of each
+  // (batch, KV head) row publish their part's maxima as 64-bit words
+  // (epoch + 1) << 32 | fp32 bits; the merge advances the epoch once per step.
+  unsigned long long* pm_words;  // [B][npart][Hq]
+  unsigned long long* pm_sync;   // [0] kPmMagic once initialised, [1] epoch (low 32 bits)
   float* part_o;           // [B][Hq][nchunk][128]
   float2* part_ml;         // [B][Hq][nchunk] (m, l)
   float* dbg_mt;           // optional [B][Hq]
@@ -35,6 +46,9 @@ struct DecodeParams {
   int art_patience;        // run-time termination: stable steps before a chunk stops (0 = off)
   float art_tau, art_phi;  // ... thresholds on the probe's norm change and 1 - cosine
   int interleaved;         // chunk c holds blocks c + j * nchunk (attend) instead of c * cb + j (dense)
+  int pm_in_grid;          // 1: pseudo-max work-groups lead the attend grid (no separate launch)
+  int pm_local;            // 1: every chunk computes the pseudo-max itself (tests the fallback)
+  unsigned long long pm_magic;  // kPmMagic keyed to the word layout (written by the merge, checked by chunks)
   int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
   float delta, sm_scale;
 };

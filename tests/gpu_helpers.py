@@ -68,22 +68,50 @@ def cache_to_host(cache):
     return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
-def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union", art=None):
+def _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, pm_mode):
     import sparse_long_context_ffd_amd as ffd
     B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
     nb = shape.max_seq_len // 64
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device="cuda")
-    if ws is None:
-        ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     dbg = {
         "m_tilde": torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda"),
         "bmax": torch.full((B, Hq, nb), float("nan"), dtype=torch.float32, device="cuda"),
         "keep": torch.full((B, Hkv, nb), 7, dtype=torch.uint8, device="cuda"),
         "tmask": torch.full((B, Hq, shape.max_seq_len), 7, dtype=torch.uint8, device="cuda"),
     }
-    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug=dbg, select=select, art=art)
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug={**dbg, "pm_mode": pm_mode},
+                    select=select, art=art)
     torch.cuda.synchronize()
     return {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
+
+
+# the pseudo-max paths one decode is run through (debug pm_mode, in order, on
+# one workspace zeroed before the first): inside the attend launch on the
+# fresh workspace (no initialised sync words, so every chunk computes the
+# pseudo-max itself), inside it again (the chunks read the words the leading
+# work-groups publish), the separate launch, and inside it with every chunk
+# forced to compute it.  Selection variants and run-time termination have the
+# separate launch only.
+PM_PATHS = (2, 2, 1, 3)
+
+
+def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union", art=None):
+    """One decode step through the C ABI.  Without a caller's workspace a
+    union step runs through every pseudo-max path (PM_PATHS), which must agree
+    bit for bit (same arithmetic, only the hand-over differs); the
+    published-words run is returned."""
+    import sparse_long_context_ffd_amd as ffd
+    if ws is not None:
+        return _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, 0)
+    ws = torch.zeros(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    if select != "union" or art is not None:
+        return _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, 0)
+    runs = [_decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, mode)
+            for mode in PM_PATHS]
+    for mode, r in zip(PM_PATHS[1:], runs[1:]):
+        for k, v in runs[0].items():
+            assert np.array_equal(v, r[k], equal_nan=True), f"pseudo-max path (pm_mode {mode}) changed {k}"
+    return runs[1]
 
 
 def gpu_dense(shape, q_dev, k_dev, v_dev, lens_dev, torch, sm_scale=SM_SCALE):

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 500
+    assert L.ffd_version() == 600
 
 
 def test_strerror_covers_codes():
@@ -92,6 +92,30 @@ def test_decode_argument_errors():
     assert _decode(s, wsb=_ws(s) - 1) == -5
     assert _decode(s, ws=None) == -5
     assert _decode(s, ws=FAKE + 8) == -3
+
+
+def test_debug_argument_errors():
+    """Debug stage masks and pseudo-max modes are validated before any launch."""
+    s = ffd.make_shape(1, 32, 8, 16384)
+    c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+    def dec(stages, pm_mode, shape=s, selection=0, art=0):
+        d = _lib.Debug(None, None, None, None, None, stages, None, pm_mode)
+        o = _lib.DecodeOpts(selection, art, 0.1, 0.1)
+        return ffd.lib().ffd_decode_attn_ex(ctypes.byref(shape), FAKE, ctypes.byref(c), FAKE, 5.0, 0.088,
+                                            ctypes.byref(o), FAKE, FAKE, _ws(shape), ctypes.byref(d), None)
+    assert dec(8, 0) == -6 and dec(-1, 0) == -6
+    assert dec(0, 4) == -6 and dec(0, -1) == -6
+    # the pseudo-max inside the attend launch needs the merge in the same call,
+    for mode in (2, 3):
+        for stages in (1, 2, 3, 4, 5):
+            assert dec(stages, mode) == -6, (stages, mode)
+        # the union selection without run-time termination,
+        assert dec(0, mode, selection=1) == -6 and dec(0, mode, selection=2) == -6
+        assert dec(0, mode, art=2) == -6
+        # and the support words of a work-group (npart * G <= 256)
+        big = ffd.make_shape(1, 8, 1, 1 << 20, local=(1 << 20) - 64)
+        assert dec(0, mode, shape=big) == -6
 
 
 def _decode_sel(shape, selection, q=FAKE, ws=FAKE):
@@ -182,8 +206,32 @@ def test_cache_and_workspace_sizes():
     assert nch == math.ceil(512 / cb)
     rows = 2 * 28
     npart = 1 + 4 + 1                 # sink block, blocks of the local window, one straddling block
-    need = rows * npart * 4 + rows * nch * 8 + rows * nch * 128 * 4
-    assert need <= ffd.workspace_bytes(s) <= need + 3 * 256
+    # sync words (16 B), in-grid pseudo-max words (8 B), separate-launch maxima
+    # (4 B), chunk (m, l) and o partials; each region 256-byte aligned
+    need = 16 + rows * npart * 8 + rows * npart * 4 + rows * nch * 8 + rows * nch * 128 * 4
+    assert need <= ffd.workspace_bytes(s) <= need + 5 * 256
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,in_grid", [(1, 32, 8, 16384, True), (1, 4, 1, 4096, True),
+                                                (1, 32, 8, 262144, False), (16, 28, 4, 32768, False),
+                                                (4, 32, 8, 131072, False)])
+def test_plan_pseudomax(B, Hq, Hkv, L, in_grid):
+    """Support parts (sink block, local-window blocks, one straddling block) and
+    the pseudo-max's placement: inside the scan + refine launch when the chunk
+    work-groups fit about one round of the device (<= 1024)."""
+    s = ffd.make_shape(B, Hq, Hkv, L)
+    n, g = ffd.plan_pseudomax(s)
+    cb, nch = ffd.plan(s)
+    assert n == 1 + 4 + 1 and g == in_grid and (nch * Hkv * B <= 1024) == in_grid
+    out = ctypes.c_int32()
+    assert ffd.lib().ffd_plan_pseudomax(ctypes.byref(s), None, ctypes.byref(out)) == -1
+    assert ffd.lib().ffd_plan_pseudomax(ctypes.byref(s), ctypes.byref(out), None) == -1
+    bad = ffd.make_shape(B, Hq, Hkv, L)
+    bad.head_dim = 64
+    assert ffd.lib().ffd_plan_pseudomax(ctypes.byref(bad), ctypes.byref(out), ctypes.byref(out)) == -2
+    # a local window wider than 256 query heads' worth of words keeps its own launch
+    wide = ffd.make_shape(1, 8, 1, 1 << 20, local=(1 << 20) - 64)
+    assert ffd.plan_pseudomax(wide)[1] is False
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,expect", [(1, 32, 8, 16384, 4), (1, 32, 8, 262144, 16),
