@@ -50,15 +50,15 @@ DENSE_BYTES = 512    # fp16 K + V per token-head
 ROTATE_TARGET = 1.5e9
 # HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
 # `bench.py --workload W --no-long --no-cpu-baseline --steps 20 --warmup 5`
-# (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the default
-# attend kernel's dispatches).  Both counters are scaled by what they read for the plain
+# (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the dispatches of
+# the attend kernel the step runs).  Both counters are scaled by what they read for the plain
 # 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088 KiB
 # for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "562604b702a7be39", "fetch": 9916.25, "write": 694.0},
-    "long_256k": {"sources": "562604b702a7be39", "fetch": 134137.38, "write": 3322.5},
+    "llama8b_16k": {"sources": "6b3c42f03e6e7d9d", "fetch": 10234.19, "write": 695.5},
+    "long_256k": {"sources": "6b3c42f03e6e7d9d", "fetch": 134230.0, "write": 3322.47},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 
