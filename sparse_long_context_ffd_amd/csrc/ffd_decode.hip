@@ -326,7 +326,8 @@ __device__ void support_tile_max(const DecodeParams& p, const QFrags<G>& qf, con
 }
 
 // the work-group's maximum per query head h < G (valid in threads tid < G)
-// from the per-lane tile maxima; `red` is [kWaves][G] in LDS
+// from the per-lane tile maxima; `red` is [kWaves][G] in LDS (a caller that
+// reuses it needs a barrier before the next call)
 template <int G>
 __device__ float support_wg_max(const float (&mx)[QFrags<G>::NT], float (&red)[kWaves][G], int tid) {
   constexpr int NT = QFrags<G>::NT;
@@ -340,7 +341,6 @@ __device__ float support_wg_max(const float (&mx)[QFrags<G>::NT], float (&red)[k
   __syncthreads();
   float m = -INFINITY;
   if (tid < G) m = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-  __syncthreads();
   return m;
 }
 
@@ -937,6 +937,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         float mx[NT];
         support_tile_max<G>(p, qf, st, L, wave, lane, mx);
         m = fmaxf(m, support_wg_max<G>(mx, pm_red, tid));
+        __syncthreads();  // pm_red is written again by the next part
       }
       if (tid < G) pm_s[tid] = m;
       __syncthreads();

@@ -189,6 +189,34 @@ def test_workspace_reuse_across_calls():
     assert np.array_equal(outs[1], outs[3]) and np.array_equal(outs[1], outs[4])
 
 
+def test_workspace_shared_by_two_shapes():
+    """One workspace used in turn by two shapes whose pseudo-max words overlap
+    in memory: the sync words are keyed to the word layout, so neither shape
+    takes the other's words (it computes the pseudo-max itself) and every call
+    matches the oracle."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    wa = Workload("share_a", 1, 4, 1, 2048, 2048, deltas=(4.0,), needles=3)
+    wb = Workload("share_b", 2, 8, 2, 1024, 1024, deltas=(4.0,), needles=3)
+    cases = []
+    for w in (wa, wb):
+        c = make_case(w, 4)
+        shape = shape_for(w)
+        cases.append((w, c, shape, gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))))
+    nbytes = max(ffd.workspace_bytes(sh) for _, _, sh, _ in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for r in range(4):
+        w, c, shape, cache = cases[r % 2]
+        say(f"shared workspace call {r} ({w.name})")
+        got = gpu_decode(shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), 4.0, torch, ws=ws)
+        G = w.group
+        for b in range(w.batch):
+            for h in range(w.kv_heads):
+                pk = orc.quantize_k(c["k"][b, h])
+                check_head(orc, c["q"][b, h * G:(h + 1) * G], pk, c["v"][b, h], int(c["seq_lens"][b]), 4.0, got,
+                           b, h, G, label=f"shared call {r} b{b} h{h}")
+
+
 def test_decode_loop_append_and_decode_in_one_graph():
     """Decode loop: one captured graph appends the step's key and value at each
     sequence's position L (ffd_append_kv), advances the device lengths, and runs
