@@ -57,8 +57,8 @@ ROTATE_TARGET = 1.5e9
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "6b3c42f03e6e7d9d", "fetch": 10234.19, "write": 695.5},
-    "long_256k": {"sources": "6b3c42f03e6e7d9d", "fetch": 134230.0, "write": 3322.47},
+    "llama8b_16k": {"sources": "7d432de42e68cd72", "fetch": 10251.56, "write": 695.5},
+    "long_256k": {"sources": "7d432de42e68cd72", "fetch": 133994.88, "write": 3322.28},
 }
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
 

@@ -302,7 +302,8 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
   // another shape are never trusted.
   const bool whole = p.stages == 0 || (p.stages & 6) == 6;
   const bool fits = (long long)pl.npart * (shape->num_q_heads / shape->num_kv_heads) <= 256;
-  const bool can = selection == FFD_SELECT_UNION && o.art_patience == 0 && whole && fits;
+  const bool grid1d = (long long)(pl.npart + pl.nchunk) * shape->num_kv_heads * shape->batch < (1ll << 31);
+  const bool can = selection == FFD_SELECT_UNION && o.art_patience == 0 && whole && fits && grid1d;
   if (pm_mode >= 2 && !can) return FFD_ERR_ARG;
   p.pm_in_grid = pm_mode >= 2 || (pm_mode == 0 && can && pm_default_in_grid(shape, pl));
   p.pm_local = pm_mode == 3;

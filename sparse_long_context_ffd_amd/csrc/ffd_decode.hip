@@ -683,18 +683,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
-  const int hkv = blockIdx.y, b = blockIdx.z;
   __shared__ uint32_t qs[G * 64];
   __shared__ float pm_s[256];
   __shared__ float pm_red[kWaves][G];
-  // with the pseudo-max in the grid, the first npart work-groups of each row
-  // compute its support parts (dispatched ahead of the row's chunks)
-  const int npg = PMG ? p.npart : 0;
-  if (PMG && (int)blockIdx.x < npg) {
-    pm_group<G>(p, blockIdx.x, hkv, b, qs, pm_red);
-    return;
+  // Without PMG the grid is (nchunk, Hkv, B).  With it the grid is 1-D: the
+  // npart * Hkv * B pseudo-max work-groups of every row first (dispatched
+  // ahead of every chunk, so that they finish while the first chunks scan),
+  // then the chunks in the same order as the 3-D grid.
+  int chunk, hkv, b;
+  if constexpr (PMG) {
+    const int n_rows = p.Hkv * p.B;
+    int w = blockIdx.x;
+    if (w < p.npart * n_rows) {
+      const int row = w / p.npart;
+      pm_group<G>(p, w - row * p.npart, row % p.Hkv, row / p.Hkv, qs, pm_red);
+      return;
+    }
+    w -= p.npart * n_rows;
+    const int row = w / p.nchunk;
+    chunk = w - row * p.nchunk;
+    hkv = row % p.Hkv;
+    b = row / p.Hkv;
+  } else {
+    chunk = blockIdx.x;
+    hkv = blockIdx.y;
+    b = blockIdx.z;
   }
-  const int chunk = (int)blockIdx.x - npg;
   // the chunk's blocks are interleaved over the sequence: block j of chunk c
   // is c + j * nchunk, so the always-kept sink and local-window blocks (and
   // any cluster of kept blocks) spread over many work-groups
@@ -1346,8 +1360,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 template <int G, int SEL, bool ART, bool PMG>
 static void launch_attend(const DecodeParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), dim3(p.nchunk + (PMG ? p.npart : 0), p.Hkv, p.B), dim3(256),
-                     AttendCfg<G>::lds_bytes(p.cb), s, p);
+  const dim3 grid = PMG ? dim3((unsigned)((p.npart + p.nchunk) * p.Hkv * p.B)) : dim3(p.nchunk, p.Hkv, p.B);
+  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), grid, dim3(256), AttendCfg<G>::lds_bytes(p.cb), s, p);
 }
 template <int G>
 static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
