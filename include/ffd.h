@@ -274,6 +274,18 @@ int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k
                           const int32_t* seq_lens, float sm_scale, void* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Measurement aid, not part of the decode path: reads the `bytes` bytes at
+ * device address `src` once, with 16-byte loads over a fixed grid of 2048
+ * work-groups, and writes to `sink` (device, FFD_STREAM_READ_SINK_BYTES bytes,
+ * 4-byte aligned) one 32-bit word per work-group: the XOR of the 32-bit words
+ * that work-group read, so the XOR over all of sink equals that of the whole
+ * buffer (0 for bytes == 0).  The time of one call gives the achievable HBM
+ * read rate beside the nominal peak.  Errors: FFD_ERR_NULL (src or sink NULL),
+ * FFD_ERR_ALIGN (src not 16-byte aligned, bytes not a multiple of 16, sink not
+ * 4-byte aligned), FFD_ERR_HIP.  Asynchronous on `stream`. */
+#define FFD_STREAM_READ_SINK_BYTES 8192
+int ffd_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Static description of an error code. */
 const char* ffd_strerror(int code);
 

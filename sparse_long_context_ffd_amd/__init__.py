@@ -20,10 +20,11 @@ from ._lib import (  # noqa: F401
     plan_pseudomax,
     quantize_k,
     strerror,
+    stream_read,
     workspace_bytes,
 )
 
 __all__ = [
     "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn",
-    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "workspace_bytes",
+    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "stream_read", "workspace_bytes",
 ]

@@ -22,8 +22,9 @@ STATUS = {
 EXPORTED = (
     "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
     "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex",
-    "ffd_dense_decode_attn", "ffd_strerror", "ffd_version",
+    "ffd_dense_decode_attn", "ffd_stream_read", "ffd_strerror", "ffd_version",
 )
+STREAM_READ_SINK_BYTES = 8192  # FFD_STREAM_READ_SINK_BYTES
 
 
 class FFDError(RuntimeError):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.ffd_decode_attn_ex.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, P(DecodeOpts),
                                          V, V, SZ, P(Debug), V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
+        L.ffd_stream_read.argtypes = [V, SZ, V, V]
         L.ffd_strerror.argtypes = [ctypes.c_int]
         L.ffd_strerror.restype = ctypes.c_char_p
         L.ffd_version.argtypes = []
@@ -270,3 +272,15 @@ def dense_decode_attn(shape: Shape, q, k, v, seq_lens, sm_scale: float, out, wor
     _check(lib().ffd_dense_decode_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_lens),
                                        float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "ffd_dense_decode_attn")
+
+
+def stream_read(src, sink, stream=None) -> None:
+    """Streaming-read probe (a measurement aid, not part of the decode path):
+    reads every byte of the device tensor `src` once; `sink` (uint8 device
+    tensor of STREAM_READ_SINK_BYTES) receives one 32-bit XOR per work-group."""
+    import torch
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    _need(sink, torch.uint8, STREAM_READ_SINK_BYTES, "sink")
+    _check(lib().ffd_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "ffd_stream_read")

@@ -102,7 +102,7 @@ bool pm_default_in_grid(const ffd_shape_t* s, const Plan& pl) {
 
 extern "C" {
 
-int ffd_version(void) { return 600; }
+int ffd_version(void) { return 700; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -345,6 +345,13 @@ int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k
   p.npart = pl.npart;
   p.sm_scale = sm_scale;
   return from_hip(ffd::launch_dense_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int ffd_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return FFD_ERR_NULL;
+  if (!aligned16(src) || (bytes & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return FFD_ERR_ALIGN;
+  static_assert(ffd::kStreamReadGroups * sizeof(uint32_t) == FFD_STREAM_READ_SINK_BYTES, "probe sink size");
+  return from_hip(ffd::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -731,14 +731,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // Thumbnail batches: per lane 8 bytes of codes (the token's row of the A
   // fragments) and one (scale, zero) pair -- token 16w + col, group ks; the
   // four pairs of a token reach its lanes through ds_bpermute in the scan.
+  // Each load instruction of a wave covers whole cache lines of data read once:
+  // non-temporal hint.
   uint2 cwA[4], cwB[4];
   uint32_t zwA[4], zwB[4];
   auto load_batch = [&](int j0, uint2 (&cw)[4], uint32_t (&zw)[4]) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int jj = min(j0 + v, nbl_cap - 1);
-      cw[v] = buf_load_b64(r_codes, (uint32_t)to.codes, (uint32_t)blk_of(jj) * kCodesBytes);
-      zw[v] = buf_load_b32(r_sz, (uint32_t)to.szt, (uint32_t)blk_of(jj) * kSzBytes);
+      cw[v] = buf_load_b64<kNonTemporal>(r_codes, (uint32_t)to.codes, (uint32_t)blk_of(jj) * kCodesBytes);
+      zw[v] = buf_load_b32<kNonTemporal>(r_sz, (uint32_t)to.szt, (uint32_t)blk_of(jj) * kSzBytes);
     }
   };
   load_batch(0, cwA, zwA);
@@ -1032,7 +1034,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   MfmaSoftmax<NT> st;
   st.init();
   {
-    // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes)
+    // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes).
+    // The residual and its scales load with the non-temporal hint (a wave's
+    // instruction covers whole lines); V keeps the default policy, since a
+    // lane's span is split over four loads and every line is read by four
+    // instructions in turn (with the hint, 25% slower).
     const uint32_t v_lane = (uint32_t)(((4 * wave + ks) * kHeadDim + 8 * col) * 4 * sizeof(uint16_t));
     const __amdgpu_buffer_rsrc_t r_res = make_rsrc(p.res + hb * kResBytes, nbc * kResBytes);
     const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
@@ -1040,8 +1046,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     auto load_block = [&](int j, RefineRegs& x) {
       const uint32_t blk = (uint32_t)blk_of(j);
 #pragma unroll
-      for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
-      x.S8 = buf_load_b64(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
+      for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64<kNonTemporal>(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
+      x.S8 = buf_load_b64<kNonTemporal>(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
 #pragma unroll
       for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
     };
@@ -1223,9 +1229,11 @@ __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
     const uint16_t* kb = p.k + (row + t_a) * kHeadDim + 8 * ks;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) Kr[g] = *reinterpret_cast<const uint4*>(kb + 32 * g);
+    // V rows: each instruction reads 4 whole 256-byte rows (non-temporal hint);
+    // a K row's lines are read by two instructions in turn (default policy)
     const uint16_t* vb = p.v + (row + 16 * wave + tp) * kHeadDim + 8 * co;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(4 * i) * kHeadDim);
+    for (int i = 0; i < 4; ++i) Vr[i] = load_b128_nt(vb + (size_t)(4 * i) * kHeadDim);
   };
   load_block(0);
   // B fragments: column col = head, k-slice ks of each group (zero past G)

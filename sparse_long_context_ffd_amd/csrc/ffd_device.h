@@ -99,15 +99,32 @@ __device__ inline float rows_sum(float v) {
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
+//
+// CPOL is the load's cache-policy field: 0, or kNonTemporal (the `nt` bit) for
+// data read exactly once whose cache lines are each covered by one load
+// instruction (a wave's loads of 64 lanes span whole lines).  On MI355X a
+// streaming read with the hint runs about 11% faster (7.0 vs 6.3 TB/s over
+// 1 GiB).  Lines that several instructions read in turn must keep the default
+// policy: with the hint each of them fetches the line again.
+constexpr int kNonTemporal = 2;
+// 16-byte global load with the non-temporal hint (same rule as above)
+__device__ inline uint4 load_b128_nt(const void* ptr) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int CPOL = 0>
 __device__ inline uint2 buf_load_b64(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, CPOL);
   return make_uint2(v[0], v[1]);
 }
+template <int CPOL = 0>
 __device__ inline uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, CPOL);
 }
+template <int CPOL = 0>
 __device__ inline uint4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CPOL);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 

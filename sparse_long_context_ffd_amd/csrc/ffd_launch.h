@@ -61,5 +61,9 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* po
                          void* codes, void* sz, void* res, void* rsc, void* vt, hipStream_t stream);
 hipError_t launch_ffd_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_dense_decode(const DecodeParams& p, hipStream_t s);
+// streaming-read probe over kStreamReadGroups work-groups; sink holds one
+// 32-bit XOR per work-group
+constexpr int kStreamReadGroups = 2048;
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
 
 }  // namespace ffd

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 600
+    assert L.ffd_version() == 700
 
 
 def test_strerror_covers_codes():
@@ -256,3 +256,15 @@ def test_layout_maps_are_bijective():
     assert np.unique(np.concatenate([sz.ravel(), sz.ravel() + 1])).size == 512
     assert np.unique(layout._RES).size == 8192 and layout._RES.max() == 8191
     assert np.unique(layout._RSC).size == 256
+
+
+def test_stream_read_argument_errors():
+    L = ffd.lib()
+    assert L.ffd_stream_read(None, 16, FAKE, None) == -1
+    assert L.ffd_stream_read(FAKE, 16, None, None) == -1
+    assert L.ffd_stream_read(FAKE + 8, 16, FAKE, None) == -3   # src not 16-byte aligned
+    assert L.ffd_stream_read(FAKE, 24, FAKE, None) == -3       # not a whole number of 16-byte words
+    assert L.ffd_stream_read(FAKE, 16, FAKE + 2, None) == -3   # sink not 4-byte aligned
+    assert _lib.STREAM_READ_SINK_BYTES == 8192
+    text = open(HEADER).read()
+    assert re.search(r"#define FFD_STREAM_READ_SINK_BYTES 8192\b", text)
