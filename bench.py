@@ -63,8 +63,8 @@ ROTATE_TARGET = 1.5e9
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "9c0a4a194672454d", "fetch": 10249.75, "write": 695.5},
-    "long_256k": {"sources": "9c0a4a194672454d", "fetch": 137564.75, "write": 3303.06},
+    "llama8b_16k": {"sources": "5e6ca527002af4c5", "fetch": 10249.5, "write": 695.5},
+    "long_256k": {"sources": "5e6ca527002af4c5", "fetch": 136671.19, "write": 2463.66},
 }
 REPLAYS = 10  # replays of the K-step graph behind the reported spread (the first is the timed one)
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"

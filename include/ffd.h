@@ -162,8 +162,9 @@ int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_by
                     size_t* res_bytes, size_t* rscale_bytes, size_t* v_bytes);
 
 /* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
- * (host call).  The workspace holds partial pseudo-maxima and per-chunk
- * attention partials; its contents need no initialisation.  It also carries a
+ * (host call; the larger of their two work splits).  The workspace holds
+ * partial pseudo-maxima and per-chunk attention partials; its contents need
+ * no initialisation.  It also carries a
  * step counter from one ffd_decode_attn call to the next: when the pseudo-max
  * runs inside the scan + refine launch (on short caches, see
  * ffd_debug_t.pm_mode) its results are tagged with that counter.  The first
@@ -173,8 +174,11 @@ int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_by
  * ordered (same stream). */
 int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
 
-/* Work split chosen for `shape`: blocks per work-group and chunks per
- * sequence (host call). */
+/* Work split ffd_decode_attn chooses for `shape`: blocks per work-group and
+ * chunks per sequence (host call).  shape->chunk_blocks > 0 forces the blocks
+ * per work-group (capped at 32, or 16 when a KV head serves more than 4 query
+ * heads); otherwise about 1380 work-groups per launch, at most 4 blocks each
+ * on short caches.  ffd_dense_decode_attn aims at about 2048 instead. */
 int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks);
 
 /* Where the pseudo-max of a whole ffd_decode_attn step (union selection, no

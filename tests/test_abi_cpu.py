@@ -212,6 +212,17 @@ def test_cache_and_workspace_sizes():
     assert need <= ffd.workspace_bytes(s) <= need + 5 * 256
 
 
+def test_workspace_covers_the_dense_split():
+    # at 256K the decode splits into 24-block chunks, the dense baseline into
+    # 16-block ones: the workspace holds the larger set of partials
+    s = ffd.make_shape(1, 32, 8, 262144)
+    assert ffd.plan(s)[0] == 24
+    rows, npart, nch_dense = 32, 6, 4096 // 16
+    need_dense = 16 + rows * npart * 8 + rows * npart * 4 + rows * nch_dense * (8 + 128 * 4)
+    assert ffd.workspace_bytes(s) >= need_dense
+    assert ffd.workspace_bytes(s) <= need_dense + 5 * 256
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,L,in_grid", [(1, 32, 8, 16384, True), (1, 4, 1, 4096, True),
                                                 (1, 32, 8, 262144, False), (16, 28, 4, 32768, False),
                                                 (4, 32, 8, 131072, False)])
@@ -234,11 +245,11 @@ def test_plan_pseudomax(B, Hq, Hkv, L, in_grid):
     assert ffd.plan_pseudomax(wide)[1] is False
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,L,expect", [(1, 32, 8, 16384, 4), (1, 32, 8, 262144, 16),
+@pytest.mark.parametrize("B,Hq,Hkv,L,expect", [(1, 32, 8, 16384, 4), (1, 32, 8, 262144, 24),
                                                (16, 28, 4, 32768, 16), (1, 4, 1, 4096, 1),
                                                (4, 32, 8, 131072, 32), (1, 1, 1, 64, 1)])
 def test_automatic_split(B, Hq, Hkv, L, expect):
-    """About 2048 work-groups per launch on long caches, up to 4 blocks per work-group on
+    """About 1380 work-groups per launch on long caches, up to 4 blocks per work-group on
     short ones; at most 32 blocks per chunk (16 when G > 4)."""
     cb, nch = ffd.plan(ffd.make_shape(B, Hq, Hkv, L))
     assert cb == expect and nch == math.ceil(L // 64 / cb)
