@@ -114,10 +114,11 @@ def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, w
     return runs[1]
 
 
-def gpu_dense(shape, q_dev, k_dev, v_dev, lens_dev, torch, sm_scale=SM_SCALE):
+def gpu_dense(shape, q_dev, k_dev, v_dev, lens_dev, torch, sm_scale=SM_SCALE, ws=None):
     import sparse_long_context_ffd_amd as ffd
     out = torch.empty((shape.batch, shape.num_q_heads, 128), dtype=torch.float16, device="cuda")
-    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     ffd.dense_decode_attn(shape, q_dev, k_dev, v_dev, lens_dev, sm_scale, out, ws)
     torch.cuda.synchronize()
     return out.float().cpu().numpy()

@@ -109,6 +109,39 @@ def test_dense_matches_oracle():
             assert ma <= 2e-3 and rel <= 1e-3
 
 
+def test_decode_and_dense_share_a_workspace_across_splits():
+    """At 64K context the decode splits into 6-block chunks and the dense
+    baseline into 4-block ones.  One workspace of ffd_workspace_bytes serves
+    both in turn; each matches the oracle and the decode repeats bit for bit."""
+    import sparse_long_context_ffd_amd as ffd
+    torch = torch_mod()
+    w = Workload("split_64k", 1, 32, 8, 65536, 65536, needles=16)
+    heads = [(0, 2), (0, 5)]
+    c = make_case(w, 0, heads=heads)
+    shape = shape_for(w)
+    assert ffd.plan(shape)[0] == 6
+    qd, kd, vd, ld = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch), dev(c["seq_lens"], torch)
+    cache = gpu_pack(shape, kd, vd)
+    ws = torch.zeros(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    say(f"shared workspace {w.name}: decode, dense, decode")
+    first = gpu_decode(shape, qd, cache, ld, 5.0, torch, ws=ws)
+    dense = gpu_dense(shape, qd, kd, vd, ld, torch, ws=ws)
+    again = gpu_decode(shape, qd, cache, ld, 5.0, torch, ws=ws)
+    for k, v in first.items():
+        assert np.array_equal(v, again[k], equal_nan=True), k
+    G = w.group
+    for b, h in heads:
+        L = int(c["seq_lens"][b])
+        pk = orc.quantize_k(c["k"][b, h])
+        check_head(orc, c["q"][b, h * G:(h + 1) * G], pk, c["v"][b, h], L, 5.0, again, b, h, G,
+                   sink=w.sink, local=w.local, label=f"split_64k b{b} h{h}")
+        ref = orc.dense_head(c["q"][b, h * G:(h + 1) * G], c["k"][b, h], c["v"][b, h], L, SM_SCALE)
+        d = dense[b, h * G:(h + 1) * G] - ref
+        ma, rel = float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
+        say(f"  dense b{b} h{h} max_abs={ma:.2e} rel={rel:.2e}")
+        assert ma <= 2e-3 and rel <= 1e-3
+
+
 def test_infinite_delta_equals_dense_over_khat():
     """delta = +inf keeps every block; the result is dense attention over K-hat."""
     torch = torch_mod()
