@@ -481,6 +481,13 @@ def main():
         torch.cuda.empty_cache()
 
     result["hbm_achievable"] = hbm_probe(torch)
+    # the attend kernels' rates against the measured streaming-read rate too
+    # (context beside `frac`, which stays against the nominal peak)
+    rd = result["hbm_achievable"]["read_gbps"]
+    result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / rd, 4)
+    if "long_context" in result:
+        ra = result["long_context"]["roofline_attend"]
+        ra["frac_of_read_probe"] = round(ra["achieved"] / rd, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, delta, c, sm_scale)
