@@ -32,7 +32,10 @@
  * unless said otherwise; the caller allocates and frees everything.  Calls
  * enqueue work on `stream` (a hipStream_t, or NULL for the null stream) and
  * return without synchronising the host.  The library keeps no state between
- * calls.  Errors are returned as negative codes; argument checks happen
+ * calls apart from two documented exceptions: the step counter a workspace
+ * carries from one ffd_decode_attn call to the next (ffd_workspace_bytes), and
+ * the static scratch array of ffd_decode_attn_noalloc.  Errors are returned
+ * as negative codes; argument checks happen
  * before any HIP call, so a non-zero return means nothing was enqueued
  * (except FFD_ERR_HIP, which reports a failed launch).
  */
@@ -54,7 +57,9 @@ enum ffd_status {
   FFD_ERR_DELTA = -4,     /* delta is NaN or -infinity                           */
   FFD_ERR_WORKSPACE = -5, /* workspace NULL or smaller than ffd_workspace_bytes  */
   FFD_ERR_ARG = -6,       /* bad scalar argument (token range, sm_scale)         */
-  FFD_ERR_HIP = -7        /* a kernel launch failed                              */
+  FFD_ERR_HIP = -7,       /* a kernel launch failed                              */
+  FFD_ERR_TOO_LARGE = -8  /* the shape needs more scratch than the static buffer  */
+                          /* of ffd_decode_attn_noalloc                          */
 };
 
 /* Problem shape.  Requirements: batch >= 1, num_kv_heads >= 1,
@@ -270,6 +275,26 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
 int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
                            const int32_t* seq_lens, float delta, float sm_scale, int32_t selection, void* out,
                            void* workspace, size_t workspace_bytes, const ffd_debug_t* debug, void* stream);
+
+/* Allocation-free ffd_decode_attn, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same step with the union selection, no run-time
+ * termination and no diagnostics, whose workspace is a static device array of
+ * FFD_NOALLOC_SCRATCH_BYTES bytes inside the library (one per GPU, held until
+ * the process ends).  The call allocates and frees nothing; the caller still
+ * owns q, the cache, seq_lens and out (same rules as ffd_decode_attn).
+ *  - A shape whose workspace (ffd_workspace_bytes' FFD part) exceeds
+ *    FFD_NOALLOC_SCRATCH_BYTES returns FFD_ERR_TOO_LARGE.
+ *  - `stream` must belong to the current device (else FFD_ERR_ARG).  The
+ *    first call on a device looks the array's address up on that device
+ *    (a host query, no allocation); make it once outside any graph capture.
+ *  - Every call on one GPU shares that GPU's array and leaves its contents
+ *    for the next: calls that overlap on one GPU (other streams, other host
+ *    threads without ordering) race and must not be issued.  Calls ordered
+ *    on one stream are safe in any sequence of shapes. */
+#define FFD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ffd_decode_attn_noalloc(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
+                            const int32_t* seq_lens, float delta, float sm_scale, void* out, void* stream);
 
 /* Dense flash-decode attention over fp16 K and V ([B][Hkv][max_seq_len][128]),
  * the speed baseline: out = softmax(q k^T * sm_scale) v over tokens [0, L).

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     append_kv,
     cache_bytes,
     decode_attn,
+    decode_attn_noalloc,
     dense_decode_attn,
     lib,
     make_shape,
@@ -25,6 +26,6 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn",
+    "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn", "decode_attn_noalloc",
     "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "stream_read", "workspace_bytes",
 ]

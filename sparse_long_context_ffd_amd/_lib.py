@@ -17,14 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libffd.so")
 FFD_OK = 0
 STATUS = {
     0: "FFD_OK", -1: "FFD_ERR_NULL", -2: "FFD_ERR_SHAPE", -3: "FFD_ERR_ALIGN", -4: "FFD_ERR_DELTA",
-    -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP",
+    -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP", -8: "FFD_ERR_TOO_LARGE",
 }
 EXPORTED = (
     "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
-    "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex",
+    "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex", "ffd_decode_attn_noalloc",
     "ffd_dense_decode_attn", "ffd_stream_read", "ffd_strerror", "ffd_version",
 )
 STREAM_READ_SINK_BYTES = 8192  # FFD_STREAM_READ_SINK_BYTES
+NOALLOC_SCRATCH_BYTES = 32 << 20  # FFD_NOALLOC_SCRATCH_BYTES
 
 
 class FFDError(RuntimeError):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
                                              V, SZ, P(Debug), V]
         L.ffd_decode_attn_ex.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, P(DecodeOpts),
                                          V, V, SZ, P(Debug), V]
+        L.ffd_decode_attn_noalloc.argtypes = [P(Shape), V, P(Cache), V, ctypes.c_float, ctypes.c_float, V, V]
         L.ffd_dense_decode_attn.argtypes = [P(Shape), V, V, V, V, ctypes.c_float, V, V, SZ, V]
         L.ffd_stream_read.argtypes = [V, SZ, V, V]
         L.ffd_strerror.argtypes = [ctypes.c_int]
@@ -257,6 +259,24 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
                                             _ptr(workspace), workspace.numel(),
                                             None if dbg is None else ctypes.byref(dbg), _stream(stream)),
                "ffd_decode_attn_select")
+
+
+def decode_attn_noalloc(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_scale: float, out,
+                        stream=None) -> None:
+    """ffd_decode_attn_noalloc: one union decode step whose workspace is the
+    library's static per-GPU scratch array (no allocation by the call)."""
+    import torch
+    rows = shape.batch * shape.num_q_heads
+    _need(q, torch.float16, rows * 128, "q")
+    _need(out, torch.float16, rows * 128, "out")
+    _need(seq_lens, torch.int32, shape.batch, "seq_lens")
+    nb = cache_bytes(shape)
+    for f in FIELDS:
+        _need(getattr(cache, f), torch.uint8, nb[f], f"cache.{f}")
+    c = cache.c_struct()
+    _check(lib().ffd_decode_attn_noalloc(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
+                                         float(delta), float(sm_scale), _ptr(out), _stream(stream)),
+           "ffd_decode_attn_noalloc")
 
 
 def dense_decode_attn(shape: Shape, q, k, v, seq_lens, sm_scale: float, out, workspace, stream=None) -> None:

@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/ffd.h"
@@ -110,7 +113,7 @@ bool pm_default_in_grid(const ffd_shape_t* s, const Plan& pl) {
 
 extern "C" {
 
-int ffd_version(void) { return 700; }
+int ffd_version(void) { return 800; }
 
 const char* ffd_strerror(int code) {
   switch (code) {
@@ -122,6 +125,7 @@ const char* ffd_strerror(int code) {
     case FFD_ERR_WORKSPACE: return "workspace missing or too small";
     case FFD_ERR_ARG: return "bad scalar argument (token range or sm_scale)";
     case FFD_ERR_HIP: return "HIP kernel launch failed";
+    case FFD_ERR_TOO_LARGE: return "shape needs more than the static scratch of ffd_decode_attn_noalloc (FFD_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown ffd status code";
   }
 }
@@ -229,9 +233,48 @@ int ffd_decode_attn_select(const ffd_shape_t* shape, const void* q, const ffd_ca
                             stream);
 }
 
-int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
-                       float delta, float sm_scale, const ffd_decode_opts_t* opts, void* out, void* workspace,
-                       size_t workspace_bytes, const ffd_debug_t* debug, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Allocation-free decode: its workspace is this static device array (one copy
+// per GPU, held until the process ends).  Host code never passes the array's
+// name to a kernel: its device address is looked up once per device.
+__device__ __align__(256) unsigned char scratch[FFD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of `scratch` on the device `stream` runs on (which must be
+// the current device); looked up with hipGetSymbolAddress on the first call
+// per device, with that device current
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FFD_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FFD_ERR_HIP;
+    if ((int)sdev != dev) return FFD_ERR_ARG;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FFD_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return FFD_OK;
+}
+
+// Shared body of the decode entry points.  With `noalloc` the workspace
+// arguments are ignored and the step runs on the static scratch array.
+int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
+                float delta, float sm_scale, const ffd_decode_opts_t* opts, void* out, void* workspace,
+                size_t workspace_bytes, const ffd_debug_t* debug, void* stream, bool noalloc) {
   ffd_decode_opts_t o = {};
   if (opts) o = *opts;
   const int32_t selection = o.selection;
@@ -253,6 +296,12 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
                              !(o.art_phi >= 0.f) || isinf(o.art_phi)))
     return FFD_ERR_ARG;
   const Plan pl = make_plan(shape);
+  if (noalloc) {
+    if (pl.total > (size_t)FFD_NOALLOC_SCRATCH_BYTES) return FFD_ERR_TOO_LARGE;
+    const int sa = scratch_address(static_cast<hipStream_t>(stream), &workspace);
+    if (sa) return sa;
+    workspace_bytes = FFD_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < pl.total) return FFD_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FFD_ERR_ALIGN;
 
@@ -320,6 +369,23 @@ int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_
   p.pm_magic = ffd::kPmMagic ^ ((unsigned long long)shape->batch << 40) ^ ((unsigned long long)shape->num_q_heads << 24) ^
                ((unsigned long long)pl.npart << 4);
   return from_hip(ffd::launch_ffd_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int ffd_decode_attn_ex(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache, const int32_t* seq_lens,
+                       float delta, float sm_scale, const ffd_decode_opts_t* opts, void* out, void* workspace,
+                       size_t workspace_bytes, const ffd_debug_t* debug, void* stream) {
+  return decode_impl(shape, q, cache, seq_lens, delta, sm_scale, opts, out, workspace, workspace_bytes, debug,
+                     stream, false);
+}
+
+int ffd_decode_attn_noalloc(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cache,
+                            const int32_t* seq_lens, float delta, float sm_scale, void* out, void* stream) {
+  return decode_impl(shape, q, cache, seq_lens, delta, sm_scale, nullptr, out, nullptr, 0, nullptr, stream, true);
 }
 
 int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k, const void* v,

@@ -31,11 +31,11 @@ def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.ffd_version() == 700
+    assert L.ffd_version() == 800
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert "unknown" not in ffd.strerror(code)
     assert "unknown" in ffd.strerror(-99)
 
@@ -279,3 +279,36 @@ def test_stream_read_argument_errors():
     assert _lib.STREAM_READ_SINK_BYTES == 8192
     text = open(HEADER).read()
     assert re.search(r"#define FFD_STREAM_READ_SINK_BYTES 8192\b", text)
+
+
+def _noalloc(shape, q=FAKE, cache=None, lens=FAKE, delta=5.0, scale=0.088, out=FAKE):
+    c = cache or _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return ffd.lib().ffd_decode_attn_noalloc(None if shape is None else ctypes.byref(shape), q, ctypes.byref(c),
+                                             lens, delta, scale, out, None)
+
+
+def test_noalloc_argument_errors():
+    """The allocation-free step validates like ffd_decode_attn, and a shape whose
+    workspace exceeds the static scratch array is refused before any HIP call."""
+    s = ffd.make_shape(1, 32, 8, 16384)
+    assert _noalloc(None) == -1
+    assert _noalloc(s, q=None) == -1
+    assert _noalloc(s, out=None) == -1
+    assert _noalloc(s, lens=None) == -1
+    assert _noalloc(s, q=FAKE + 8) == -3
+    assert _noalloc(s, delta=float("nan")) == -4
+    assert _noalloc(s, scale=0.0) == -6
+    assert _noalloc(ffd.make_shape(1, 32, 8, 1000)) == -2
+    big = ffd.make_shape(64, 64, 8, 262144)
+    assert ffd.workspace_bytes(big) > _lib.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big) == -8
+    assert "FFD_NOALLOC_SCRATCH_BYTES" in ffd.strerror(-8)
+    # the header's size is the binding's
+    text = open(HEADER).read()
+    assert re.search(r"#define FFD_NOALLOC_SCRATCH_BYTES \(32u << 20\)", text)
+    assert _lib.NOALLOC_SCRATCH_BYTES == 32 << 20
+    # every workload of the benchmark fits
+    from synthetic import WORKLOADS
+    for w in WORKLOADS.values():
+        sw = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
+        assert ffd.workspace_bytes(sw) <= _lib.NOALLOC_SCRATCH_BYTES, w.name
