@@ -274,38 +274,44 @@ def decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: 
 
 # --------------------------------------------------------------------------
 # run-time termination of the refine stream (the ART page, "Attention
-# Run-time Termination", Method sections 2.2-2.4), applied to each chunk
+# Run-time Termination", Method sections 2.1-2.4)
 # --------------------------------------------------------------------------
 ART_PROBE = 8  # probe = the first 8 output channels of the group's first query head
 
 
-def chunk_blocks(nblk: int, cb: int, nchunk: int) -> List[List[int]]:
-    """Blocks of each chunk under the interleaved split: chunk c holds blocks
-    c, c + nchunk, c + 2 nchunk, ... (at most cb of them, all below nblk)."""
-    return [[c + j * nchunk for j in range(cb) if c + j * nchunk < nblk] for c in range(min(nchunk, nblk))]
+def art_streams(nblk: int, stream_blocks: int) -> List[List[int]]:
+    """The streams of one sequence: a streaming (split-KV) attention unit
+    accumulates a contiguous run of KV blocks, so stream s holds blocks
+    [s * stream_blocks, (s + 1) * stream_blocks), cut at the sequence end.
+    The partition depends only on the sequence length and the call's
+    stream_blocks."""
+    if stream_blocks < 1:
+        raise ValueError("stream_blocks must be >= 1")
+    return [list(range(s, min(s + stream_blocks, nblk))) for s in range(0, nblk, stream_blocks)]
 
 
 def art_decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray, L: int,
-                    delta: float, sm_scale: float, cb: int, nchunk: int, tau: float, phi: float,
+                    delta: float, sm_scale: float, stream_blocks: int, tau: float, phi: float,
                     patience: int, sink: int = 64, local: int = 256,
                     keep: Optional[np.ndarray] = None) -> Dict[str, object]:
-    """FFD decode where every chunk's stream of kept blocks may stop early.
+    """FFD decode where every stream of kept blocks may stop early.
 
-    Each chunk (the unit that streams blocks into one running output) visits
-    its kept blocks in increasing order.  After block t it takes the probe
+    Each stream (``art_streams``) visits its kept blocks in increasing order,
+    folding each into a running output.  After block t it takes the probe
     x_t = the first ART_PROBE channels of its running normalised output for
     the group's first query head, and from the second block on compares it
     with the previous probe:
         d_scale = | ||x_t|| - ||x_{t-1}|| |,   d_dir = 1 - cos(x_t, x_{t-1})
     (d_dir = 1 when either norm is 0).  A step is stable when d_scale < tau
-    and d_dir < phi; after `patience` consecutive stable steps the chunk skips
-    its remaining blocks.  Every query head of the group follows the chunk's
-    decision.  The output is exact attention over the union of the visited
-    blocks (the per-chunk outputs merge by log-sum-exp, which is order
-    invariant).  patience <= 0 disables the stop.
+    and d_dir < phi; after `patience` consecutive stable steps the stream
+    skips its remaining blocks.  Every query head of the group follows the
+    stream's decision.  The output is exact attention over the union of the
+    visited blocks (the streams' outputs merge by log-sum-exp, which is order
+    invariant).  Block 0 (forced kept) is the first block of stream 0, so it
+    is always evaluated.  patience <= 0 disables the stop.
 
     Returns the decode_head fields plus ``visited`` [nblk] bool, ``streams``
-    (per chunk: blocks visited, blocks kept, and per step (d_scale, d_dir)).
+    (per stream: blocks, blocks kept, blocks visited, per step (d_scale, d_dir)).
     """
     base = decode_head(q16, pk, V16, L, delta, sm_scale, sink, local, keep=keep)
     keep = base["keep"]
@@ -315,7 +321,7 @@ def art_decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray,
     Vf = np.asarray(V16, dtype=np.float64)[:L]
     visited = np.zeros(nblk, dtype=bool)
     streams = []
-    for blocks in chunk_blocks(nblk, cb, nchunk):
+    for blocks in art_streams(nblk, stream_blocks):
         kept = [b for b in blocks if keep[b]]
         m = np.full(G, -np.inf)
         lsum = np.zeros(G)
@@ -349,6 +355,22 @@ def art_decode_head(q16: np.ndarray, pk: Dict[str, np.ndarray], V16: np.ndarray,
     tok = np.repeat(visited, BLOCK)[:L]
     out = attend_tokens(s, V16[:L], np.nonzero(tok)[0])
     return {**base, "visited": visited, "streams": streams, "out": out}
+
+
+def art_decode(q: np.ndarray, pk: Dict[str, np.ndarray], v: np.ndarray, seq_lens: Sequence[int],
+               delta: float, sm_scale: float, stream_blocks: int, tau: float, phi: float, patience: int,
+               sink: int = 64, local: int = 256,
+               heads: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], Dict[str, object]]:
+    """art_decode_head for every (b, kv_head) (or the listed ones) of a batch;
+    shapes as in ``decode``."""
+    B, Hq, _ = q.shape
+    Hkv = v.shape[1]
+    G = Hq // Hkv
+    todo = [(b, h) for b in range(B) for h in range(Hkv)] if heads is None else list(heads)
+    return {(b, h): art_decode_head(q[b, h * G:(h + 1) * G], {f: a[b, h] for f, a in pk.items()}, v[b, h],
+                                    int(seq_lens[b]), delta, sm_scale, stream_blocks, tau, phi, patience,
+                                    sink, local)
+            for b, h in todo}
 
 
 def dense_head(q16: np.ndarray, keys: np.ndarray, V16: np.ndarray, L: int,
