@@ -294,8 +294,8 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     }
 
 
-# run-time termination of each chunk's refine stream timed beside the selection
-# variants: (tau, phi, patience)
+# run-time termination of the refine streams (the default 16-block streams)
+# timed beside the selection variants: (tau, phi, patience)
 ART = (0.05, 0.01, 1)
 
 

@@ -65,10 +65,13 @@ enum ffd_status {
 /* Problem shape.  Requirements: batch >= 1, num_kv_heads >= 1,
  * num_q_heads = G * num_kv_heads with 1 <= G <= 8, head_dim == 128,
  * block == 64, sink >= 0, local >= 0, sink + local > 0 (the pseudo-max needs
- * at least one support token), max_seq_len a positive multiple of 64,
+ * at least one support token), max_seq_len a positive multiple of 64 below
+ * 2^24 (the kernels address one head's 256 bytes of values per token with
+ * 32-bit offsets),
  * chunk_blocks >= 0 (0 = library choice; otherwise the number of 64-token
  * blocks one work-group scans and refines, capped at 32 for G <= 4 and 16
- * above; it changes only the summation order of the result), batch and
+ * above; it changes only the summation order of the result, and run-time
+ * termination ignores it), batch and
  * num_kv_heads at most 65535 (launch-grid dimensions). */
 typedef struct ffd_shape {
   int32_t batch;
@@ -166,10 +169,11 @@ enum ffd_selection { FFD_SELECT_UNION = 0, FFD_SELECT_HEAD_BLOCK = 1, FFD_SELECT
 int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_bytes,
                     size_t* res_bytes, size_t* rscale_bytes, size_t* v_bytes);
 
-/* Workspace bytes ffd_decode_attn and ffd_dense_decode_attn need for `shape`
- * (host call; the larger of their two work splits).  The workspace holds
- * partial pseudo-maxima and per-chunk attention partials; its contents need
- * no initialisation.  It also carries a
+/* Workspace bytes ffd_decode_attn, ffd_decode_attn_select, ffd_decode_attn_ex
+ * with run-time termination at the default stream length, and
+ * ffd_dense_decode_attn need for `shape` (host call; the largest of their
+ * work splits).  The workspace holds partial pseudo-maxima and per-chunk
+ * attention partials; its contents need no initialisation.  It also carries a
  * step counter from one ffd_decode_attn call to the next: when the pseudo-max
  * runs inside the scan + refine launch (on short caches, see
  * ffd_debug_t.pm_mode) its results are tagged with that counter.  The first
@@ -241,27 +245,45 @@ int ffd_decode_attn(const ffd_shape_t* shape, const void* q, const ffd_cache_t* 
                     void* stream);
 
 /* Options of ffd_decode_attn_ex.
- *  selection     enum ffd_selection
- *  art_patience  run-time termination of the refine stream (the ART page,
- *                "Attention Run-time Termination", Method 2.2-2.4), applied
- *                to every work-group's stream of kept blocks.  The stream
- *                visits its kept blocks in increasing order (the interleaved
- *                split of ffd_plan: chunk c holds blocks c, c + n_chunks, ...).
- *                After each block it takes the probe x = the first 8 channels
- *                of the running normalised output of the group's first query
- *                head; from the second block on, a step is stable when
- *                | ||x|| - ||x_prev|| | < art_tau and 1 - cos(x, x_prev) <
- *                art_phi, and after art_patience consecutive stable steps the
- *                stream skips its remaining blocks (all query heads of the
- *                group follow it).  0 turns it off; > 0 requires
- *                FFD_SELECT_UNION and finite art_tau, art_phi >= 0.
+ *  selection          enum ffd_selection
+ *  art_patience       run-time termination of the refine streams (the ART
+ *                     page, "Attention Run-time Termination", Method 2.1-2.4:
+ *                     a streaming attention unit stops folding in KV blocks
+ *                     once its running output is stable).  Stream s of each
+ *                     (sequence, KV head) is the contiguous run of blocks
+ *                     [s * S, (s + 1) * S), S = art_stream_blocks, cut at the
+ *                     sequence end; it visits its kept blocks in increasing
+ *                     order (block 0, forced kept, opens stream 0).  After
+ *                     each block it takes the probe x = the first 8 channels
+ *                     of the running normalised output of the group's first
+ *                     query head; from the second block on, a step is stable
+ *                     when | ||x|| - ||x_prev|| | < art_tau and
+ *                     1 - cos(x, x_prev) < art_phi, and after art_patience
+ *                     consecutive stable steps the stream skips its
+ *                     remaining blocks (all query heads of the group follow
+ *                     it).  The visited blocks depend only on the sequence,
+ *                     the query and these options (not on the batch, the
+ *                     cache capacity or shape->chunk_blocks).  0 turns it off;
+ *                     > 0 requires FFD_SELECT_UNION, finite art_tau,
+ *                     art_phi >= 0, and 1 <= S <= 32 (16 when a KV head
+ *                     serves more than 4 query heads).
+ *  art_stream_blocks  S, the stream length in 64-token blocks
+ *                     (0 = FFD_ART_STREAM_BLOCKS_DEFAULT); also the blocks per
+ *                     work-group of such a call.
  * The debug tmask marks the tokens of the blocks actually refined. */
+#define FFD_ART_STREAM_BLOCKS_DEFAULT 16
 typedef struct ffd_decode_opts {
   int32_t selection;
   int32_t art_patience;
   float art_tau;
   float art_phi;
+  int32_t art_stream_blocks;
 } ffd_decode_opts_t;
+
+/* Workspace bytes one ffd_decode_attn_ex call with options `opts` (NULL =
+ * defaults) needs (host call): the figure for another art_stream_blocks than
+ * the default.  FFD_ERR_ARG for an out-of-range stream length. */
+int ffd_workspace_bytes_ex(const ffd_shape_t* shape, const ffd_decode_opts_t* opts, size_t* bytes);
 
 /* ffd_decode_attn with options (NULL = defaults: union selection, no
  * run-time termination); invalid options return FFD_ERR_ARG. */

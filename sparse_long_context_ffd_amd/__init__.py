@@ -23,9 +23,11 @@ from ._lib import (  # noqa: F401
     strerror,
     stream_read,
     workspace_bytes,
+    workspace_bytes_ex,
 )
 
 __all__ = [
     "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn", "decode_attn_noalloc",
     "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "stream_read", "workspace_bytes",
+    "workspace_bytes_ex",
 ]

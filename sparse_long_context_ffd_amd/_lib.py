@@ -20,7 +20,7 @@ STATUS = {
     -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP", -8: "FFD_ERR_TOO_LARGE",
 }
 EXPORTED = (
-    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_workspace_bytes_ex", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
     "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex", "ffd_decode_attn_noalloc",
     "ffd_dense_decode_attn", "ffd_stream_read", "ffd_strerror", "ffd_version",
 )
@@ -55,7 +55,10 @@ SELECTIONS = {"union": 0, "head_block": 1, "head_token": 2}
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("selection", ctypes.c_int32), ("art_patience", ctypes.c_int32), ("art_tau", ctypes.c_float),
-                ("art_phi", ctypes.c_float)]
+                ("art_phi", ctypes.c_float), ("art_stream_blocks", ctypes.c_int32)]
+
+
+ART_STREAM_BLOCKS_DEFAULT = 16  # FFD_ART_STREAM_BLOCKS_DEFAULT
 
 
 _lib = None
@@ -71,6 +74,7 @@ def lib() -> ctypes.CDLL:
         P, V, SZ, I32 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
         L.ffd_cache_bytes.argtypes = [P(Shape), P(SZ), P(SZ), P(SZ), P(SZ), P(SZ)]
         L.ffd_workspace_bytes.argtypes = [P(Shape), P(SZ)]
+        L.ffd_workspace_bytes_ex.argtypes = [P(Shape), P(DecodeOpts), P(SZ)]
         L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_plan_pseudomax.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
@@ -121,6 +125,26 @@ def cache_bytes(shape: Shape) -> dict:
 def workspace_bytes(shape: Shape) -> int:
     n = ctypes.c_size_t()
     _check(lib().ffd_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)), "ffd_workspace_bytes")
+    return n.value
+
+
+def _opts(select: str = "union", art=None) -> "DecodeOpts":
+    if select not in SELECTIONS:
+        raise ValueError(f"unknown selection {select!r}")
+    if art is None:
+        return DecodeOpts(SELECTIONS[select], 0, 0.0, 0.0, 0)
+    tau, phi, patience = art[:3]
+    stream_blocks = art[3] if len(art) > 3 else 0
+    return DecodeOpts(SELECTIONS[select], int(patience), float(tau), float(phi), int(stream_blocks))
+
+
+def workspace_bytes_ex(shape: Shape, select: str = "union", art=None) -> int:
+    """Workspace bytes of one decode call with these options (``art`` as in
+    decode_attn)."""
+    n = ctypes.c_size_t()
+    o = _opts(select, art)
+    _check(lib().ffd_workspace_bytes_ex(ctypes.byref(shape), ctypes.byref(o), ctypes.byref(n)),
+           "ffd_workspace_bytes_ex")
     return n.value
 
 
@@ -220,8 +244,9 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
                 art: Optional[Tuple[float, float, int]] = None) -> None:
     """One decode step; ``select`` is "union" (ffd_decode_attn) or a selection
     variant "head_block" / "head_token" (ffd_decode_attn_select); ``art`` =
-    (tau, phi, patience) turns on the run-time termination of each chunk's
-    refine stream (ffd_decode_attn_ex)."""
+    (tau, phi, patience[, stream_blocks]) turns on the run-time termination
+    of each refine stream (ffd_decode_attn_ex; stream_blocks 0 or absent =
+    the default length)."""
     import torch
     rows = shape.batch * shape.num_q_heads
     _need(q, torch.float16, rows * 128, "q")
@@ -238,9 +263,7 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
                     debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)),
                     _ptr(debug.get("tmask")), int(debug.get("pm_mode", 0)))
     if art is not None:
-        if select not in SELECTIONS:
-            raise ValueError(f"unknown selection {select!r}")
-        opts = DecodeOpts(SELECTIONS[select], int(art[2]), float(art[0]), float(art[1]))
+        opts = _opts(select, art)
         _check(lib().ffd_decode_attn_ex(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),
                                         float(delta), float(sm_scale), ctypes.byref(opts), _ptr(out),
                                         _ptr(workspace), workspace.numel(),

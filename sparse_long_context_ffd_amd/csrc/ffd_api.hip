@@ -45,6 +45,9 @@ int check_shape(const ffd_shape_t* s) {
   if (s->sink < 0 || s->local < 0 || s->chunk_blocks < 0) return FFD_ERR_SHAPE;
   if (s->sink == 0 && s->local == 0) return FFD_ERR_SHAPE;  // the pseudo-max needs a support set
   if (s->max_seq_len < 64 || s->max_seq_len % 64 != 0) return FFD_ERR_SHAPE;
+  // the kernels address one head's blocks with 32-bit byte offsets (its
+  // values take max_seq_len * 256 bytes)
+  if ((long long)s->max_seq_len * ffd::kHeadDim * 2 > 0xFFFFFFFFll) return FFD_ERR_SHAPE;
   // batch and KV heads are launch-grid dimensions (at most 65535 each)
   if (s->batch > 65535 || s->num_kv_heads > 65535) return FFD_ERR_SHAPE;
   return FFD_OK;
@@ -58,13 +61,17 @@ struct Plan {
 // Work split: one work-group per chunk of cb blocks (4 waves, one 16-token tile
 // of every block each).  cb is sized for about kTargetGroups work-groups per
 // launch and bounded by the LDS the per-block estimates of a chunk need.
-Plan make_plan(const ffd_shape_t* s, long long target = kTargetGroups) {
+// `fixed_cb` > 0 sets the blocks per work-group (run-time termination: the
+// call's stream length) in place of the shape's choice.
+Plan make_plan(const ffd_shape_t* s, long long target = kTargetGroups, int fixed_cb = 0) {
   Plan p;
   const int G = s->num_q_heads / s->num_kv_heads;
   const int cb_max = G <= 4 ? 32 : 16;
   p.nblk_cap = s->max_seq_len / 64;
   long long cb;
-  if (s->chunk_blocks > 0) {
+  if (fixed_cb > 0) {
+    cb = fixed_cb;
+  } else if (s->chunk_blocks > 0) {
     cb = s->chunk_blocks;
   } else {
     // about kTargetGroups work-groups on long caches; short caches take up to
@@ -109,6 +116,19 @@ bool pm_default_in_grid(const ffd_shape_t* s, const Plan& pl) {
   return fits && (long long)pl.nchunk * s->num_kv_heads * s->batch <= kPmgMaxGroups;
 }
 
+// run-time termination: the call's stream length (0 = the default), or -1
+// when it is out of range for the shape
+int art_stream_blocks(const ffd_shape_t* s, const ffd_decode_opts_t& o) {
+  const int G = s->num_q_heads / s->num_kv_heads;
+  const int sb = o.art_stream_blocks == 0 ? FFD_ART_STREAM_BLOCKS_DEFAULT : o.art_stream_blocks;
+  return (sb < 1 || sb > (G <= 4 ? 32 : 16)) ? -1 : sb;
+}
+
+// the plan a decode call with options `o` runs
+Plan decode_plan(const ffd_shape_t* s, const ffd_decode_opts_t& o) {
+  return o.art_patience > 0 ? make_plan(s, kTargetGroups, art_stream_blocks(s, o)) : make_plan(s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,9 +168,23 @@ int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes) {
   const int st = check_shape(shape);
   if (st) return st;
   if (!bytes) return FFD_ERR_NULL;
-  // one workspace serves both the FFD decode and the dense baseline
+  // one workspace serves the FFD decode, the dense baseline and run-time
+  // termination with the default stream length
   const size_t a = make_plan(shape).total, d = make_plan(shape, kDenseTargetGroups).total;
+  const size_t r = make_plan(shape, kTargetGroups, FFD_ART_STREAM_BLOCKS_DEFAULT).total;
   *bytes = a > d ? a : d;
+  if (r > *bytes) *bytes = r;
+  return FFD_OK;
+}
+
+int ffd_workspace_bytes_ex(const ffd_shape_t* shape, const ffd_decode_opts_t* opts, size_t* bytes) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!bytes) return FFD_ERR_NULL;
+  ffd_decode_opts_t o = {};
+  if (opts) o = *opts;
+  if (o.art_patience > 0 && art_stream_blocks(shape, o) < 0) return FFD_ERR_ARG;
+  *bytes = decode_plan(shape, o).total;
   return FFD_OK;
 }
 
@@ -293,9 +327,9 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
     return FFD_ERR_ARG;
   if (o.art_patience < 0) return FFD_ERR_ARG;
   if (o.art_patience > 0 && (selection != FFD_SELECT_UNION || !(o.art_tau >= 0.f) || isinf(o.art_tau) ||
-                             !(o.art_phi >= 0.f) || isinf(o.art_phi)))
+                             !(o.art_phi >= 0.f) || isinf(o.art_phi) || art_stream_blocks(shape, o) < 0))
     return FFD_ERR_ARG;
-  const Plan pl = make_plan(shape);
+  const Plan pl = decode_plan(shape, o);
   if (noalloc) {
     if (pl.total > (size_t)FFD_NOALLOC_SCRATCH_BYTES) return FFD_ERR_TOO_LARGE;
     const int sa = scratch_address(static_cast<hipStream_t>(stream), &workspace);
@@ -307,7 +341,7 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
 
   ffd::DecodeParams p = {};
   p.select = selection;
-  p.interleaved = 1;
+  p.interleaved = o.art_patience > 0 ? 0 : 1;  // a termination stream is a contiguous chunk
   p.art_patience = o.art_patience;
   p.art_tau = o.art_tau;
   p.art_phi = o.art_phi;

@@ -709,12 +709,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     hkv = blockIdx.y;
     b = blockIdx.z;
   }
-  // the chunk's blocks are interleaved over the sequence: block j of chunk c
+  // The chunk's blocks are interleaved over the sequence: block j of chunk c
   // is c + j * nchunk, so the always-kept sink and local-window blocks (and
-  // any cluster of kept blocks) spread over many work-groups
+  // any cluster of kept blocks) spread over many work-groups.  Under run-time
+  // termination a chunk is one stream of the call: the contiguous blocks
+  // c * cb .. c * cb + cb - 1 (cb = the call's stream length).
   const int nck = p.nchunk;
-  auto blk_of = [&](int j) { return chunk + j * nck; };
-  const int nbl_cap = min(p.cb, (p.nblk_cap - chunk + nck - 1) / nck);
+  auto blk_of = [&](int j) { return ART ? chunk * p.cb + j : chunk + j * nck; };
+  auto blocks_below = [&](int n) {  // blocks of the chunk below block index n
+    return ART ? max(0, min(p.cb, n - chunk * p.cb)) : min(p.cb, (n - chunk + nck - 1) / nck);
+  };
+  const int nbl_cap = blocks_below(p.nblk_cap);
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
   const TileOffsets to(wave, lane);
@@ -774,8 +779,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
-  if (chunk >= nblk) return;
-  const int nbl = min(p.cb, (nblk - chunk + nck - 1) / nck);
+  const int nbl = blocks_below(nblk);
+  if (nbl <= 0) return;
   const bool dbg_bmax = p.dbg_bmax != nullptr;
   // Rows past the sequence end get estimate -inf only where it can matter:
   // with a local window the block holding the last token is always kept (and

@@ -95,22 +95,53 @@ def _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, sele
 PM_PATHS = (2, 2, 1, 3)
 
 
+def ws_bytes(shape, select="union", art=None):
+    """Workspace bytes for a decode call with these options."""
+    import sparse_long_context_ffd_amd as ffd
+    return max(ffd.workspace_bytes(shape), ffd.workspace_bytes_ex(shape, select, art))
+
+
+def production_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union",
+                      art=None):
+    """The call as a user makes it (and as bench.py times it): no debug
+    buffers, the library's own pseudo-max placement and launch split.
+    Returns the fp16 output as float32 numpy."""
+    import sparse_long_context_ffd_amd as ffd
+    out = torch.full((shape.batch, shape.num_q_heads, 128), float("nan"), dtype=torch.float16, device="cuda")
+    if ws is None:
+        ws = torch.full((ws_bytes(shape, select, art),), 0x5A, dtype=torch.uint8, device="cuda")
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, select=select, art=art)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
 def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, ws=None, select="union", art=None):
     """One decode step through the C ABI.  Without a caller's workspace a
     union step runs through every pseudo-max path (PM_PATHS), which must agree
     bit for bit (same arithmetic, only the hand-over differs); the
-    published-words run is returned."""
+    published-words run is returned.  The production call (no debug buffers,
+    default placement) then runs twice on a fresh junk-filled workspace -- its
+    first call on a workspace, then one that uses what the first published --
+    and both outputs must equal the debug run's bit for bit, so every oracle
+    comparison of the returned output also covers the production call."""
     import sparse_long_context_ffd_amd as ffd
     if ws is not None:
         return _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, 0)
-    ws = torch.zeros(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes(shape, select, art), dtype=torch.uint8, device="cuda")
     if select != "union" or art is not None:
-        return _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, 0)
+        got = _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, 0)
+        prod = production_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, select=select, art=art)
+        assert np.array_equal(prod, got["out"]), f"production call ({select}, art={art}) differs from the debug run"
+        return got
     runs = [_decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, mode)
             for mode in PM_PATHS]
     for mode, r in zip(PM_PATHS[1:], runs[1:]):
         for k, v in runs[0].items():
             assert np.array_equal(v, r[k], equal_nan=True), f"pseudo-max path (pm_mode {mode}) changed {k}"
+    pws = torch.full((ffd.workspace_bytes(shape),), 0x5A, dtype=torch.uint8, device="cuda")
+    for i in range(2):
+        prod = production_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws=pws)
+        assert np.array_equal(prod, runs[1]["out"]), f"production call {i} differs from the debug run"
     return runs[1]
 
 

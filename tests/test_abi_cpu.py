@@ -61,6 +61,7 @@ def test_shape_validation():
         dict(max_seq_len=1000), dict(max_seq_len=0), dict(sink=-1), dict(local=-1),
         dict(sink=0, local=0), dict(chunk_blocks=-2), dict(batch=0), dict(num_kv_heads=0),
         dict(batch=65536), dict(num_q_heads=65536, num_kv_heads=65536),  # grid dimensions
+        dict(max_seq_len=1 << 24), dict(max_seq_len=(1 << 24) + 64),      # 32-bit block offsets
     ]
     for kw in bad:
         args = dict(batch=1, num_q_heads=32, num_kv_heads=8, max_seq_len=16384)
@@ -72,6 +73,8 @@ def test_shape_validation():
         assert ffd.lib().ffd_workspace_bytes(ctypes.byref(s), ctypes.byref(n)) == -2, kw
         assert _decode(s, wsb=1 << 30) == -2, kw
     assert ffd.lib().ffd_workspace_bytes(None, ctypes.byref(ctypes.c_size_t())) == -1
+    # the longest cache the 32-bit offsets address
+    assert ffd.workspace_bytes(ffd.make_shape(1, 4, 1, (1 << 24) - 64)) > 0
 
 
 def test_decode_argument_errors():
@@ -134,11 +137,11 @@ def test_decode_select_argument_errors():
     assert set(_lib.SELECTIONS.values()) == {0, 1, 2}
 
 
-def _decode_ex(shape, opts, q=FAKE):
+def _decode_ex(shape, opts, q=FAKE, wsb=None):
     c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
     return ffd.lib().ffd_decode_attn_ex(ctypes.byref(shape), q, ctypes.byref(c), FAKE, 5.0, 0.088,
-                                        None if opts is None else ctypes.byref(opts), FAKE, FAKE, _ws(shape),
-                                        None, None)
+                                        None if opts is None else ctypes.byref(opts), FAKE, FAKE,
+                                        _ws(shape) if wsb is None else wsb, None, None)
 
 
 def test_decode_ex_option_errors():
@@ -149,6 +152,34 @@ def test_decode_ex_option_errors():
         assert _decode_ex(s, bad) == -6, (bad.selection, bad.art_patience, bad.art_tau, bad.art_phi)
     for good in (None, O(0, 0, 0.0, 0.0), O(0, 2, 0.05, 0.01), O(2, 0, -1.0, math.nan)):
         assert _decode_ex(s, good, q=None) == -1       # valid options: the pointer checks still run first
+
+
+def test_art_stream_length_and_workspace():
+    """The run-time termination stream length is validated per group size and
+    sizes the workspace of the call (ffd_workspace_bytes_ex)."""
+    O = _lib.DecodeOpts
+    s4 = ffd.make_shape(1, 32, 8, 16384)        # G = 4: up to 32 blocks per stream
+    s8 = ffd.make_shape(1, 64, 8, 16384)        # G = 8: up to 16
+    for sh, bad in ((s4, 33), (s4, -1), (s8, 17)):
+        assert _decode_ex(sh, O(0, 1, 0.1, 0.1, bad), wsb=1 << 30) == -6, bad
+        n = ctypes.c_size_t()
+        assert ffd.lib().ffd_workspace_bytes_ex(ctypes.byref(sh), ctypes.byref(O(0, 1, 0.1, 0.1, bad)),
+                                                ctypes.byref(n)) == -6
+    for sh, good in ((s4, 32), (s4, 1), (s8, 16), (s8, 0)):
+        assert _decode_ex(sh, O(0, 1, 0.1, 0.1, good), q=None) == -1
+    # partials: one per stream of 4-block chunks; the default length fits ffd_workspace_bytes
+    rows, nblk = 32, 16384 // 64
+    assert ffd.workspace_bytes_ex(s4, art=(0.1, 0.1, 1)) <= ffd.workspace_bytes(s4)
+    one = ffd.workspace_bytes_ex(s4, art=(0.1, 0.1, 1, 1))
+    assert one >= rows * nblk * (128 + 2) * 4 > ffd.workspace_bytes(s4)
+    # the stream length is ignored without termination; opts NULL = the plain step
+    assert ffd.workspace_bytes_ex(s4) == ffd.workspace_bytes_ex(s4, art=None)
+    n = ctypes.c_size_t()
+    assert ffd.lib().ffd_workspace_bytes_ex(ctypes.byref(s4), None, ctypes.byref(n)) == 0
+    assert n.value == ffd.workspace_bytes_ex(s4) <= ffd.workspace_bytes(s4)
+    # a call with a too-small workspace for its stream length is refused
+    assert _decode_ex(s4, O(0, 1, 0.1, 0.1, 1), wsb=ffd.workspace_bytes(s4)) == -5
+    assert _decode_ex(s4, O(0, 1, 0.1, 0.1, 1), q=None, wsb=one) == -1
 
 
 def test_dense_and_pack_argument_errors():

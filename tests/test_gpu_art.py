@@ -1,5 +1,7 @@
-"""GPU parity of the run-time termination of each chunk's refine stream
-(ffd_decode_attn_ex with art_patience > 0) against the fp64 oracle.
+"""GPU parity of the run-time termination of the refine streams
+(ffd_decode_attn_ex with art_patience > 0) against the fp64 oracle.  Stream s
+of a sequence is the contiguous run of art_stream_blocks blocks starting at
+block s * art_stream_blocks; the oracle takes that length from the call.
 
 A stream's stop step follows from its sequence of (norm change, 1 - cosine)
 values; where every one of the oracle's values lies farther than ART_BAND
@@ -19,18 +21,28 @@ from tests.gpu_helpers import (ATOL, BAND, RTOL_L2, SM_SCALE, dev, gpu_decode, g
 
 pytestmark = pytest.mark.gpu
 ART_BAND = 1e-4
+ART_STREAM_BLOCKS_DEFAULT = 16
 
 
-def _run_art(w, seed, delta, art, heads=None, chunk_blocks=0):
-    import sparse_long_context_ffd_amd as ffd
+def _visited(got, b, h, G, L, label):
+    """Blocks the GPU refined for (b, kv head h): token flags of the group's
+    query heads, which must all agree."""
+    nb = (L + 63) // 64
+    tm = got["tmask"][b, h * G:(h + 1) * G, :L]
+    assert (tm == tm[0]).all(), f"{label} query heads of a group visited different blocks"
+    return tm[0, np.arange(nb) * 64] == 1
+
+
+def _run_art(w, seed, delta, art, heads=None, stream_blocks=0):
     torch = torch_mod()
     tau, phi, patience = art
+    sb = stream_blocks or ART_STREAM_BLOCKS_DEFAULT
     c = make_case(w, seed, heads=heads)
-    shape = shape_for(w, chunk_blocks)
-    cb, nchunk = ffd.plan(shape)
+    shape = shape_for(w)
     cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
-    say(f"art {w.name} seed={seed} delta={delta} cb={cb} art={art} heads={heads}")
-    got = gpu_decode(shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), delta, torch, art=art)
+    say(f"art {w.name} seed={seed} delta={delta} stream_blocks={sb} art={art} heads={heads}")
+    got = gpu_decode(shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), delta, torch,
+                     art=(tau, phi, patience, stream_blocks))
     G = w.group
     todo = heads if heads is not None else [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
     totals = {"streams": 0, "pinned": 0, "stopped": 0, "visited": 0, "kept": 0}
@@ -45,13 +57,9 @@ def _run_art(w, seed, delta, art, heads=None, chunk_blocks=0):
         pkp, pdp = mask_pins(base)
         assert not (pkp & ~keep).any() and not (pdp & keep).any(), f"{label} mask mismatch on pinned blocks"
         assert np.abs(got["m_tilde"][b, h * G:(h + 1) * G] - base["m_tilde"]).max() <= BAND
-        # blocks the GPU refined: token flags of the group's query heads (all equal)
-        tm = got["tmask"][b, h * G:(h + 1) * G, :L]
-        assert (tm == tm[0]).all(), f"{label} query heads of a group visited different blocks"
-        first = np.arange(nb) * 64
-        visited = tm[0, first] == 1
+        visited = _visited(got, b, h, G, L, label)
         assert (visited <= keep).all(), f"{label} refined a dropped block"
-        r = orc.art_decode_head(q16, pk, V16, L, delta, SM_SCALE, cb, nchunk, tau, phi, patience, keep=keep)
+        r = orc.art_decode_head(q16, pk, V16, L, delta, SM_SCALE, sb, tau, phi, patience, keep=keep)
         for st in r["streams"]:
             totals["streams"] += 1
             totals["stopped"] += len(st["visited"]) < len(st["kept"])
@@ -73,21 +81,22 @@ def _run_art(w, seed, delta, art, heads=None, chunk_blocks=0):
 
 @pytest.mark.parametrize("art", [(0.05, 0.01, 1), (0.02, 0.005, 2), (0.2, 0.05, 3)])
 def test_art_tiny_long_streams(art):
-    """delta = inf keeps every block; 16 blocks per chunk make long streams."""
-    t = _run_art(WORKLOADS["tiny_h4x1_4k"], 0, math.inf, art, chunk_blocks=16)
+    """delta = inf keeps every block; 16-block streams are long."""
+    t = _run_art(WORKLOADS["tiny_h4x1_4k"], 0, math.inf, art, stream_blocks=16)
     if art[2] == 1:
         assert t["stopped"] > 0 and t["visited"] < t["kept"]
 
 
 @pytest.mark.parametrize("seed", [1, 2])
 def test_art_tiny_top_delta(seed):
-    _run_art(WORKLOADS["tiny_h4x1_4k"], seed, 2.0, (0.05, 0.01, 1), chunk_blocks=8)
+    _run_art(WORKLOADS["tiny_h4x1_4k"], seed, 2.0, (0.05, 0.01, 1), stream_blocks=8)
 
 
-def test_art_llama8b_16k_production_split():
-    """The 16K shape in its production split (4 blocks per chunk): the stop
-    logic runs after every refined block."""
-    _run_art(WORKLOADS["llama8b_16k"], 0, 5.0, (0.05, 0.01, 1), heads=[(0, 0), (0, 5)])
+@pytest.mark.parametrize("stream_blocks", [0, 4, 32])
+def test_art_llama8b_16k(stream_blocks):
+    """The 16K shape at the default stream length and at 4 and 32 blocks."""
+    _run_art(WORKLOADS["llama8b_16k"], 0, 5.0, (0.05, 0.01, 1), heads=[(0, 0), (0, 5)],
+             stream_blocks=stream_blocks)
 
 
 def test_art_long_256k_sampled():
@@ -97,6 +106,50 @@ def test_art_long_256k_sampled():
 
 def test_art_group_sizes_and_ragged_batch():
     _run_art(WORKLOADS["qwen7b_b16_16k32k"], 0, math.inf, (0.02, 0.005, 2), heads=[(4, 1)])
-    for G, L in [(1, 3000), (8, 2500), (3, 1000)]:
+    for G, L, sb in [(1, 3000, 16), (8, 2500, 16), (3, 1000, 1), (5, 4000, 7)]:
         w = Workload(f"art_g{G}_l{L}", 2, 2 * G, 2, 4096, L, needles=4)
-        _run_art(w, 0, math.inf, (0.05, 0.01, 1), chunk_blocks=16)
+        _run_art(w, 0, math.inf, (0.05, 0.01, 1), stream_blocks=sb)
+
+
+def test_art_streams_follow_the_call_not_the_batch_or_capacity():
+    """The same sequences and queries visit the same blocks and give the same
+    output bits alone (batch 1), inside a batch of 16, and at two cache
+    capacities: the streams come from the call's stream length, not from the
+    occupancy split of the launch."""
+    import sparse_long_context_ffd_amd as ffd
+    torch = torch_mod()
+    G, Hkv, L, delta, art = 4, 2, 3000, 3.0, (0.05, 0.01, 1, 4)
+    w1 = Workload("art_same_b1", 1, G * Hkv, Hkv, 3008, L, needles=4)
+    c1 = make_case(w1, 7)
+    runs = []
+    for B, L_cap, b0 in [(1, 3008, 0), (1, 8192, 0), (16, 4096, 9), (16, 8192, 2)]:
+        rng = np.random.default_rng([B, L_cap])
+        q = rng.standard_normal((B, G * Hkv, 128)).astype(np.float16)
+        k = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
+        v = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
+        lens = rng.integers(1, L_cap, size=B, endpoint=True).astype(np.int32)
+        q[b0], k[b0, :, :L], v[b0, :, :L], lens[b0] = c1["q"][0], c1["k"][0, :, :L], c1["v"][0, :, :L], L
+        shape = ffd.make_shape(B, G * Hkv, Hkv, L_cap)
+        cache = gpu_pack(shape, dev(k, torch), dev(v, torch))
+        say(f"art same sequence: B={B} L_cap={L_cap} at b={b0} (plan {ffd.plan(shape)})")
+        got = gpu_decode(shape, dev(q, torch), cache, dev(lens, torch), delta, torch, art=art)
+        runs.append((got["out"][b0], [_visited(got, b0, h, G, L, f"B{B} L_cap{L_cap} h{h}") for h in range(Hkv)],
+                     got["keep"][b0, :, :(L + 63) // 64].astype(bool)))
+    out0, vis0, keep0 = runs[0]
+    for out, vis, keep in runs[1:]:
+        assert np.array_equal(keep, keep0), "kept blocks depend on the batch or the capacity"
+        assert np.array_equal(out, out0), "output bits depend on the batch or the capacity"
+        for a, b in zip(vis, vis0):
+            assert np.array_equal(a, b), "visited blocks depend on the batch or the capacity"
+    # and they are the oracle's
+    for h in range(Hkv):
+        pk = orc.quantize_k(c1["k"][0, h])
+        r = orc.art_decode_head(c1["q"][0, h * G:(h + 1) * G], pk, c1["v"][0, h], L, delta, SM_SCALE, 4, *art[:3],
+                                keep=keep0[h])
+        robust = all(abs(ds - art[0]) > ART_BAND and abs(dd - art[1]) > ART_BAND
+                     for st in r["streams"] for ds, dd in st["steps"])
+        if robust:
+            assert np.array_equal(vis0[h], r["visited"]), f"h{h}: visited blocks differ from the oracle's"
+        d = out0[h * G:(h + 1) * G] - orc.decode_head(c1["q"][0, h * G:(h + 1) * G], pk, c1["v"][0, h], L, delta,
+                                                      SM_SCALE, keep=vis0[h])["out"]
+        assert np.abs(d).max() <= ATOL

@@ -25,7 +25,7 @@ def test_select_tiny(select, seed):
 
 @pytest.mark.parametrize("select", SELECTS)
 def test_select_llama8b_16k_sampled(select):
-    """The headline 16K shape in its production launch configuration."""
+    """The headline 16K shape (the production call, without debug buffers, must give the same bits)."""
     st = _run(WORKLOADS["llama8b_16k"], 0, [5.0], heads=[(0, 0), (0, 3), (0, 7)], select=select)
     assert all(s["attended_frac"] < s["keep_frac"] for s in st), "variant attends as much as the union"
 
