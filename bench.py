@@ -11,9 +11,12 @@ flash-decode kernel timed beside it.
 Timing: the decode step is captured in a HIP graph, as the pages do with
 CUDA graphs to remove CPU launch overhead: W untimed warm-up steps, then one
 graph of exactly K steps replayed between two events and bracketed by
-torch.cuda.synchronize().  Per-layer caches are rotated (step i reads copy
-i mod R) so that the bytes touched between two visits of the same copy exceed
-the 256 MB last-level cache.  The fused scan + refine kernel is then timed
+torch.cuda.synchronize().  The 256 MB last-level cache (MALL) is defeated two
+ways: per-layer caches are rotated (step i reads copy i mod R), with R sized
+from the bytes one step reads so that more than 1.1 GB is read between two
+visits of one copy (R = ceil(1.1 GB / bytes per step) + 1), and before every
+timed replay a 1 GiB device copy (1 GiB read, 1 GiB written) evicts what the
+previous replay left, outside the events.  The fused scan + refine kernel is then timed
 alone: a graph of K back-to-back launches of it (stage mask 2) on the same
 stream; its mean launch duration is the roofline denominator.  When the
 pseudo-max runs inside that launch it needs the merge of the same step (which
@@ -34,6 +37,16 @@ Roofline: achieved = algorithmic bytes of the fused kernel per launch (48 B per
 token-head scanned + 392 B per kept token-head refined, + 184 B per support
 token-head when the pseudo-max runs inside it) / its mean duration, against
 the 8 TB/s HBM3E peak.
+
+Legs beside the headline 16K step (all timed the same way):
+  long_context   the 256K shape (delta 5) and the dense baseline; its
+                 scan_only object is the same shape at delta = -1e30 (only the
+                 forced sink/local blocks refined), so the attend kernel is
+                 almost only the 2-bit thumbnail stream;
+  batched_qwen   the batch of 16 Qwen2.5-7B-like heads at 16K-32K (delta 7);
+  stress         the low-sparsity B=4 x 128K shape (delta 7);
+  context_sweep  FFD and dense at 16K, 32K, 64K, 128K and 256K with the
+                 Llama-8B-like heads, with least-squares slopes.
 """
 from __future__ import annotations
 
@@ -56,7 +69,9 @@ SCAN_BYTES = 48      # 2-bit codes 32 B + (scale, zero) 16 B per token-head
 REFINE_BYTES = 392   # int8 residual 128 B + rscale 8 B + fp16 V 256 B per kept token-head
 PSEUDO_BYTES = 184   # packed K (codes, scale/zero, residual, rscale) per support token-head
 DENSE_BYTES = 512    # fp16 K + V per token-head
-ROTATE_TARGET = 1.5e9
+TOUCH_BETWEEN_VISITS = 1.1e9  # bytes read between two visits of one rotated cache copy
+ROTATE_BUDGET = 48e9          # device bytes the rotated copies of one leg may take
+FLUSH_BYTES = 1 << 30         # the pre-replay copy: 1 GiB read + 1 GiB written
 # HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
 # `bench.py --workload W --no-long --no-cpu-baseline --steps 20 --warmup 5`
 # (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the dispatches of
@@ -115,9 +130,34 @@ def graph_of(calls, torch):
     return g
 
 
-def timed_replay(g, torch) -> float:
-    """Replay a captured graph between two events; returns milliseconds."""
+def copies_for(read_bytes_per_step: int, stored_bytes: int) -> int:
+    """Rotated cache copies R: more than TOUCH_BETWEEN_VISITS bytes are read
+    between two visits of one copy when R - 1 steps run in between, within
+    ROTATE_BUDGET of device memory (never fewer than 2)."""
+    r = math.ceil(TOUCH_BETWEEN_VISITS / max(int(read_bytes_per_step), 1)) + 1
+    cap = max(2, int(ROTATE_BUDGET // max(int(stored_bytes), 1)))
+    return int(max(2, min(r, cap, 512)))
+
+
+class Flush:
+    """Evicts the last-level cache between timed replays: a device-to-device
+    copy of FLUSH_BYTES (its own 2 GiB of buffers, read and written once)."""
+
+    def __init__(self, torch):
+        self.src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
+
+def timed_replay(g, torch, flush=None) -> float:
+    """Replay a captured graph between two events (after `flush`, outside the
+    events); returns milliseconds."""
     torch.cuda.synchronize()
+    if flush is not None:
+        flush()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     g.replay()
@@ -176,7 +216,10 @@ def prepare(w, seed, torch):
     return c, {k: to_dev(v, torch) for k, v in c.items()}
 
 
-def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=False):
+def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, flush, with_variants=False, extras=True):
+    """Time the FFD decode step of workload `w` (graph of `steps` steps over
+    rotated cache copies) and its attend kernel alone; with `extras` also the
+    eager launches, the decode loop with append, and the cache-warm step."""
     import sparse_long_context_ffd_amd as ffd
     shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
     base = ffd.PackedCache(shape)
@@ -206,25 +249,30 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
         attend_bytes += PSEUDO_BYTES * support
 
     layer_bytes = sum(n for n in ffd.cache_bytes(shape).values())
-    R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
+    R = copies_for(step_bytes, layer_bytes)
     layers = [base] + [base.clone() for _ in range(R - 1)]
-    log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} rotate R={R} ({R * layer_bytes / 1e9:.2f} GB)")
+    log(f"ffd {w.name} delta={delta}: keep={keep_frac:.4f} reads {step_bytes / 1e6:.1f} MB/step, rotate R={R} "
+        f"({R * layer_bytes / 1e9:.2f} GB stored, {(R - 1) * step_bytes / 1e9:.2f} GB read between visits)")
 
     def step(i, stages=0, select="union", art=None):
         ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
                         debug={"stages": stages} if stages else None, select=select, art=art)
 
-    # eager launches (host-bound for short contexts), for reference
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    eager_us = t0.elapsed_time(t1) * 1e3 / steps
+    res = {}
+    if extras:
+        # eager launches (host-bound for short contexts), for reference
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        flush()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        res["eager_us_per_step"] = t0.elapsed_time(t1) * 1e3 / steps
     # the decode step as the pages run it: captured in a graph (K steps over the
     # rotated layers per replay); W warm-up steps replayed first
     g_warm, g_steps = graph_of([lambda i=i: step(i) for i in range(warmup)], torch), \
@@ -235,71 +283,77 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, with_variants=Fa
     else:
         g_attend = graph_of([lambda i=i: step(i, stages=2) for i in range(steps)], torch)
         g_merge = None
-    # decode loop: each step first appends one token per sequence (its last one,
-    # rewritten with the same key and value, so the cache and the work stay fixed)
-    last = d["seq_lens"].long() - 1
-    bidx = torch.arange(w.batch, device="cuda")
-    k_last = d["k"][bidx, :, last].contiguous()          # [B][Hkv][128]
-    v_last = d["v"][bidx, :, last].contiguous()
-    pos = (d["seq_lens"] - 1).to(torch.int32).contiguous()
-
-    def loop_step(i):
-        ffd.append_kv(shape, k_last, v_last, pos, layers[i % R])
-        step(i)
-
-    g_loop = graph_of([lambda i=i: loop_step(i) for i in range(steps)], torch)
-    # the same K steps on one layer's cache (no rotation): the cache-warm time,
-    # with the layer's bytes partly resident in the 256 MB last-level cache
-    g_warmcache = graph_of([lambda: ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, out, ws)
-                            for _ in range(steps)], torch)
     g_warm.replay()
     g_steps.replay()  # untimed: a graph's first launch also uploads it to the device
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    total_ms = timed_replay(g_steps, torch)
+    total_ms = timed_replay(g_steps, torch, flush)
     wall = time.perf_counter() - wall0
     # spread: the same K-step graph replayed again, one mean per replay
-    rep_us = sorted([total_ms * 1e3 / steps] + [timed_replay(g_steps, torch) * 1e3 / steps
+    rep_us = sorted([total_ms * 1e3 / steps] + [timed_replay(g_steps, torch, flush) * 1e3 / steps
                                                  for _ in range(REPLAYS - 1)])
     g_attend.replay()
-    attend_total_ms = timed_replay(g_attend, torch)
+    attend_total_ms = timed_replay(g_attend, torch, flush)
     if g_merge is not None:
         g_merge.replay()
-        attend_total_ms -= timed_replay(g_merge, torch)
-    g_loop.replay()
-    loop_total_ms = timed_replay(g_loop, torch)
-    g_warmcache.replay()
-    warmcache_ms = timed_replay(g_warmcache, torch)
+        attend_total_ms -= timed_replay(g_merge, torch, flush)
+    del g_warm, g_attend, g_merge
+    if extras:
+        # decode loop: each step first appends one token per sequence (its last
+        # one, rewritten with the same key and value, so the cache and the work
+        # stay fixed)
+        last = d["seq_lens"].long() - 1
+        bidx = torch.arange(w.batch, device="cuda")
+        k_last = d["k"][bidx, :, last].contiguous()          # [B][Hkv][128]
+        v_last = d["v"][bidx, :, last].contiguous()
+        pos = (d["seq_lens"] - 1).to(torch.int32).contiguous()
+
+        def loop_step(i):
+            ffd.append_kv(shape, k_last, v_last, pos, layers[i % R])
+            step(i)
+
+        g_loop = graph_of([lambda i=i: loop_step(i) for i in range(steps)], torch)
+        g_loop.replay()
+        res["loop_us_per_step"] = timed_replay(g_loop, torch, flush) * 1e3 / steps
+        del g_loop
+        # the same K steps on one layer's cache (no rotation, no flush): the
+        # cache-warm time, with the layer's bytes partly resident in the MALL
+        g_warmcache = graph_of([lambda: ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, out,
+                                                        ws) for _ in range(steps)], torch)
+        g_warmcache.replay()
+        res["cache_warm_us_per_step"] = timed_replay(g_warmcache, torch) * 1e3 / steps
+        del g_warmcache
     us_step = total_ms * 1e3 / steps
     attend_us = attend_total_ms * 1e3 / steps
-    variants = selection_variants(shape, w, delta, d, base, ws, sm_scale, torch, steps, step) if with_variants else None
-    return {
+    variants = selection_variants(shape, w, delta, d, base, ws, sm_scale, torch, steps, step, flush) \
+        if with_variants else None
+    res.update({
         "variants": variants,
         "us_per_step": us_step,
         "replay_spread": {"replays": REPLAYS, "p10": round(float(np.percentile(rep_us, 10)), 3),
                           "median": round(float(np.median(rep_us)), 3),
                           "p90": round(float(np.percentile(rep_us, 90)), 3)},
         "wall_us_per_step": wall * 1e6 / steps,
-        "eager_us_per_step": eager_us,
         "attend_us_mean": attend_us,
         "pm_in_grid": pm_in_grid,
-        "loop_us_per_step": loop_total_ms * 1e3 / steps,
-        "cache_warm_us_per_step": warmcache_ms * 1e3 / steps,
         "keep_fraction": keep_frac,
         "attend_bytes": attend_bytes,
         "step_bytes": step_bytes,
         "tokens": tok_total,
         "layers_rotated": R,
+        "read_between_visits": (R - 1) * step_bytes,
         "plan": ffd.plan(shape),
-    }
+    })
+    return res
 
 
-# run-time termination of the refine streams (the default 16-block streams)
-# timed beside the selection variants: (tau, phi, patience)
-ART = (0.05, 0.01, 1)
+# run-time termination timed beside the selection variants: (tau, phi,
+# patience, stream length); streams of 4 blocks give the 16K step as many
+# work-groups as the union split
+ART = (0.05, 0.01, 1, 4)
 
 
-def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, step):
+def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, step, flush):
     """Per-head block sets, per-token masking and run-time termination: time
     per step, fraction of (query head, token) pairs attended, and the output's
     deviation from full attention over K-hat (delta = +inf).  The selection
@@ -321,8 +375,8 @@ def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, st
         diff = (o.float() - full.float())
         g = graph_of([lambda i=i: step(i, **kw) for i in range(steps)], torch)
         g.replay()
-        us = timed_replay(g, torch) * 1e3 / steps
-        res[sel] = {**({"tau_phi_patience": list(ART)} if sel == "art" else {}),
+        us = timed_replay(g, torch, flush) * 1e3 / steps
+        res[sel] = {**({"tau_phi_patience_stream_blocks": list(ART)} if sel == "art" else {}),
                     "us_per_step": round(us, 3), "attended_frac": round(att, 5),
                     "max_abs_vs_full": round(diff.abs().max().item(), 6),
                     "rel_l2_vs_full": round((diff.norm() / full.float().norm()).item(), 6)}
@@ -330,15 +384,17 @@ def selection_variants(shape, w, delta, d, cache, ws, sm_scale, torch, steps, st
     return res
 
 
-def measure_dense(w, steps, warmup, d, torch, sm_scale):
+def measure_dense(w, steps, warmup, d, torch, sm_scale, flush):
     import sparse_long_context_ffd_amd as ffd
     shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
     ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
     layer_bytes = (d["k"].numel() + d["v"].numel()) * 2
-    R = int(min(64, max(1, math.ceil(ROTATE_TARGET / layer_bytes))))
+    byts = DENSE_BYTES * int(d["seq_lens"].sum().item()) * w.kv_heads
+    R = copies_for(byts, layer_bytes)
     ks = [d["k"]] + [d["k"].clone() for _ in range(R - 1)]
     vs = [d["v"]] + [d["v"].clone() for _ in range(R - 1)]
+
     def step(i):
         ffd.dense_decode_attn(shape, d["q"], ks[i % R], vs[i % R], d["seq_lens"], sm_scale, out, ws)
 
@@ -346,10 +402,70 @@ def measure_dense(w, steps, warmup, d, torch, sm_scale):
     g_steps = graph_of([lambda i=i: step(i) for i in range(steps)], torch)
     g_warm.replay()
     g_steps.replay()  # untimed: a graph's first launch also uploads it to the device
-    us = timed_replay(g_steps, torch) * 1e3 / steps
-    byts = DENSE_BYTES * int(d["seq_lens"].sum().item()) * w.kv_heads
-    del ks, vs
-    return {"us_per_step": us, "bytes": byts, "gbps": byts / us / 1e3, "layers_rotated": R}
+    us = timed_replay(g_steps, torch, flush) * 1e3 / steps
+    del ks, vs, g_warm, g_steps
+    return {"us_per_step": us, "bytes": byts, "gbps": byts / us / 1e3, "layers_rotated": R,
+            "read_between_visits": (R - 1) * byts}
+
+
+def roofline_of(r, workload):
+    """The attend kernel's roofline entry of one measure_ffd result."""
+    ach = r["attend_bytes"] / (r["attend_us_mean"] * 1e3)
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes(workload),
+            "bytes_per_launch": r["attend_bytes"], "attend_kernel_us": round(r["attend_us_mean"], 3)}
+
+
+def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True, scan_only=False):
+    """One workload beside the headline: FFD step and attend kernel (roofline),
+    the dense baseline, and optionally the scan-only variant (delta = -1e30)."""
+    c, d = prepare(w, seed, torch)
+    r = measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, flush, extras=False)
+    out = {"workload": w.name, "delta": delta, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+           "seq_len_max": int(c["seq_lens"].max()), "tokens_per_kv_head": int(c["seq_lens"].sum()),
+           "us_per_step": round(r["us_per_step"], 3), "us_per_step_spread": r["replay_spread"],
+           "keep_fraction": round(r["keep_fraction"], 5),
+           "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
+           "roofline_attend": roofline_of(r, w.name), "layers_rotated": r["layers_rotated"],
+           "read_between_visits_gb": round(r["read_between_visits"] / 1e9, 3), "chunk_blocks": r["plan"][0]}
+    if scan_only:
+        so = measure_ffd(w, -1e30, steps, warmup, c, d, torch, sm_scale, flush, extras=False)
+        out["scan_only"] = {"delta": -1e30, "keep_fraction": round(so["keep_fraction"], 5),
+                            "us_per_step": round(so["us_per_step"], 3), "roofline_attend": roofline_of(so, None),
+                            "layers_rotated": so["layers_rotated"]}
+    if dense:
+        dn = measure_dense(w, max(10, steps // 2), min(warmup, 5), d, torch, sm_scale, flush)
+        out.update({"dense_us_per_step": round(dn["us_per_step"], 3), "dense_gbps": round(dn["gbps"], 1),
+                    "dense_layers_rotated": dn["layers_rotated"],
+                    "speedup_vs_dense": round(dn["us_per_step"] / r["us_per_step"], 3)})
+    del c, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def sweep_workload(L):
+    """The Llama-8B-like decode layer (B=1, Hq=32, Hkv=8, delta 5) at context L,
+    with the needle count of the 16K and 256K workloads' rule 16 * sqrt(L / 16K)."""
+    from synthetic import Workload
+    return Workload(f"llama8b_{L // 1024}k", 1, 32, 8, L, L, deltas=(5.0,),
+                    needles=int(round(16 * math.sqrt(L / 16384))))
+
+
+def slope(xs, ys):
+    """Least-squares slope of ys over xs."""
+    x, y = np.asarray(xs, float), np.asarray(ys, float)
+    return float(np.polyfit(x, y, 1)[0])
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(w, delta, c, sm_scale, budget_s=10.0):
@@ -377,7 +493,10 @@ def cpu_baseline(w, delta, c, sm_scale, budget_s=10.0):
     return {"value": med * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
             "sample": f"numpy fp64 oracle decode step over all {w.batch * w.kv_heads} KV heads of {w.name} "
                       f"(delta={delta}, pack excluded), median of {len(times)} steps",
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": platform.processor() or platform.machine()}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+LEGS = ("long", "qwen", "stress", "sweep")
 
 
 def main():
@@ -388,7 +507,10 @@ def main():
     ap.add_argument("--workload", default="llama8b_16k")
     ap.add_argument("--delta", type=float, default=None)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-long", action="store_true", help="skip the 256K FFD vs dense leg")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help=f"comma-separated legs beside the headline (of {', '.join(LEGS)}; '' for none)")
+    ap.add_argument("--no-long", action="store_true", help="skip every leg beside the headline")
+    ap.add_argument("--no-variants", action="store_true", help="skip the selection-variant timings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=256,
                     help="size of one plain device-to-device copy done before timing; profiles scale "
@@ -397,6 +519,11 @@ def main():
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
               file=sys.stderr)
+        sys.exit(2)
+    legs = [] if args.no_long else [x for x in args.legs.split(",") if x]
+    unknown = set(legs) - set(LEGS)
+    if unknown:
+        print(f"unknown legs {sorted(unknown)}", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -418,9 +545,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    flush = Flush(torch)
     c, d = prepare(w, args.seed, torch)
-    r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale, with_variants=True)
-    dense = measure_dense(w, args.steps, args.warmup, d, torch, sm_scale)
+    r = measure_ffd(w, delta, args.steps, args.warmup, c, d, torch, sm_scale, flush,
+                    with_variants=not args.no_variants)
+    dense = measure_dense(w, args.steps, args.warmup, d, torch, sm_scale, flush)
     achieved = r["attend_bytes"] / (r["attend_us_mean"] * 1e3)
     result = {
         "metric": METRIC,
@@ -438,7 +567,9 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "seq_len": int(c["seq_lens"].max()), "delta": delta, "sink": w.sink, "local": w.local,
                    "head_dim": 128, "block": 64, "keep_fraction": round(r["keep_fraction"], 5),
-                   "layers_rotated": r["layers_rotated"], "chunk_blocks": r["plan"][0]},
+                   "layers_rotated": r["layers_rotated"],
+                   "read_between_visits_gb": round(r["read_between_visits"] / 1e9, 3),
+                   "chunk_blocks": r["plan"][0]},
         "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
         "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
         "us_per_step_spread": r["replay_spread"],
@@ -448,6 +579,7 @@ def main():
         "cache_warm_us_per_step": round(r["cache_warm_us_per_step"], 3),
         "selection_variants": r["variants"],
         "dense_us_per_step": round(dense["us_per_step"], 3),
+        "dense_layers_rotated": dense["layers_rotated"],
         "speedup_vs_dense": round(dense["us_per_step"] / r["us_per_step"], 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_bytes(w.name),
@@ -457,37 +589,56 @@ def main():
     }
     del d
     torch.cuda.empty_cache()
-
-    if not args.no_long:
-        wl = WORKLOADS["long_256k"]
-        cl, dl = prepare(wl, args.seed, torch)
-        rl = measure_ffd(wl, wl.deltas[0], max(20, args.steps // 4), args.warmup, cl, dl, torch, sm_scale)
-        dn = measure_dense(wl, max(10, args.steps // 8), 5, dl, torch, sm_scale)
-        ach = rl["attend_bytes"] / (rl["attend_us_mean"] * 1e3)
-        result["long_context"] = {
-            "workload": wl.name, "delta": wl.deltas[0], "us_per_step": round(rl["us_per_step"], 3),
-            "us_per_step_spread": rl["replay_spread"],
-            "keep_fraction": round(rl["keep_fraction"], 5), "attend_kernel_us": round(rl["attend_us_mean"], 3),
-            "decode_loop_us_per_step": round(rl["loop_us_per_step"], 3),
-            "cache_warm_us_per_step": round(rl["cache_warm_us_per_step"], 3),
-            "effective_gbps": round(rl["step_bytes"] / (rl["us_per_step"] * 1e3), 1),
-            "roofline_attend": {"achieved": round(ach, 1), "frac": round(ach / HBM_PEAK_GBPS, 4),
-                                "traffic": traffic_bytes(wl.name), "bytes_per_launch": rl["attend_bytes"]},
-            "dense_us_per_step": round(dn["us_per_step"], 3), "dense_gbps": round(dn["gbps"], 1),
-            "speedup_vs_dense": round(dn["us_per_step"] / rl["us_per_step"], 3),
-            "layers_rotated": rl["layers_rotated"], "chunk_blocks": rl["plan"][0],
-        }
-        del dl
-        torch.cuda.empty_cache()
+    steps_leg = max(20, args.steps // 4)
+    warm_leg = min(args.warmup, 10)
+    if "long" in legs:
+        result["long_context"] = leg("long_context", WORKLOADS["long_256k"], WORKLOADS["long_256k"].deltas[0],
+                                     steps_leg, warm_leg, args.seed, torch, sm_scale, flush, scan_only=True)
+    if "qwen" in legs:
+        wq = WORKLOADS["qwen7b_b16_16k32k"]
+        result["batched_qwen"] = leg("batched_qwen", wq, wq.deltas[0], steps_leg, warm_leg, args.seed, torch,
+                                     sm_scale, flush)
+    if "stress" in legs:
+        wst = WORKLOADS["stress_b4_128k"]
+        result["stress"] = leg("stress", wst, wst.deltas[0], steps_leg, warm_leg, args.seed, torch, sm_scale,
+                               flush)
+    if "sweep" in legs:
+        pts = []
+        for L in (16384, 32768, 65536, 131072, 262144):
+            if L == 16384 and w.name == "llama8b_16k" and delta == 5.0:
+                pt = {"seq_len": L, "us_per_step": result["value"], "keep_fraction": result["config"]["keep_fraction"],
+                      "attend_kernel_us": result["attend_kernel_us"], "dense_us_per_step": result["dense_us_per_step"]}
+            elif L == 262144 and "long_context" in result:
+                lc = result["long_context"]
+                pt = {"seq_len": L, "us_per_step": lc["us_per_step"], "keep_fraction": lc["keep_fraction"],
+                      "attend_kernel_us": lc["roofline_attend"]["attend_kernel_us"],
+                      "dense_us_per_step": lc["dense_us_per_step"]}
+            else:
+                x = leg("sweep", sweep_workload(L), 5.0, steps_leg, warm_leg, args.seed, torch, sm_scale, flush)
+                pt = {"seq_len": L, "us_per_step": x["us_per_step"], "keep_fraction": x["keep_fraction"],
+                      "attend_kernel_us": x["roofline_attend"]["attend_kernel_us"],
+                      "dense_us_per_step": x["dense_us_per_step"]}
+            pt["speedup_vs_dense"] = round(pt["dense_us_per_step"] / pt["us_per_step"], 3)
+            pts.append(pt)
+        xs = [p["seq_len"] / 1024 for p in pts]
+        result["context_sweep"] = {
+            "workload": "Llama-8B-like heads (B=1, Hq=32, Hkv=8, delta 5), 16 * sqrt(L / 16K) needles per KV head",
+            "points": pts,
+            "slope_us_per_1k_tokens": {"ffd": round(slope(xs, [p["us_per_step"] for p in pts]), 4),
+                                       "dense": round(slope(xs, [p["dense_us_per_step"] for p in pts]), 4)}}
 
     result["hbm_achievable"] = hbm_probe(torch)
     # the attend kernels' rates against the measured streaming-read rate too
     # (context beside `frac`, which stays against the nominal peak)
     rd = result["hbm_achievable"]["read_gbps"]
     result["roofline"]["frac_of_read_probe"] = round(result["roofline"]["achieved"] / rd, 4)
-    if "long_context" in result:
-        ra = result["long_context"]["roofline_attend"]
-        ra["frac_of_read_probe"] = round(ra["achieved"] / rd, 4)
+    for k in ("long_context", "batched_qwen", "stress"):
+        if k in result:
+            ra = result[k]["roofline_attend"]
+            ra["frac_of_read_probe"] = round(ra["achieved"] / rd, 4)
+            if "scan_only" in result[k]:
+                so = result[k]["scan_only"]["roofline_attend"]
+                so["frac_of_read_probe"] = round(so["achieved"] / rd, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, delta, c, sm_scale)

@@ -49,3 +49,33 @@ def test_digest_ignores_comments_not_code(tmp_path, monkeypatch):
     assert bench.kernel_digest() == d0  # comments and whitespace do not count
     src.write_text(text.replace("kWaves", "kWavez"))
     assert bench.kernel_digest() != d0  # code does
+
+
+def test_rotation_reads_more_than_a_gigabyte_between_visits():
+    """R copies: R - 1 steps of reads between two visits of one copy exceed
+    TOUCH_BETWEEN_VISITS (> 1 GB, four times the 256 MB MALL)."""
+    import bench
+    assert bench.TOUCH_BETWEEN_VISITS > 1e9
+    for read, stored in [(20.5e6, 57.7e6), (273e6, 923e6), (1.07e9, 1.07e9), (6.3e6, 57.7e6), (2e9, 2e9)]:
+        R = bench.copies_for(read, stored)
+        assert R >= 2
+        assert (R - 1) * read >= bench.TOUCH_BETWEEN_VISITS
+        assert R * stored <= max(bench.ROTATE_BUDGET, 2 * stored)
+    # the memory budget caps the copies (and then says so in the log, not silently)
+    assert bench.copies_for(1e3, 10e9) == int(bench.ROTATE_BUDGET // 10e9)
+
+
+def test_sweep_workloads_match_the_16k_and_256k_needle_counts():
+    import bench
+    from synthetic import WORKLOADS
+    for name, L in (("llama8b_16k", 16384), ("long_256k", 262144)):
+        w, s = WORKLOADS[name], bench.sweep_workload(L)
+        assert (s.batch, s.q_heads, s.kv_heads, s.max_len, s.seq_len, s.needles) == \
+               (w.batch, w.q_heads, w.kv_heads, w.max_len, w.seq_len, w.needles)
+    assert [bench.sweep_workload(L).needles for L in (32768, 65536, 131072)] == [23, 32, 45]
+
+
+def test_unknown_leg_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--legs", "long,nope"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "nope" in r.stderr
