@@ -37,16 +37,37 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), *srcs, "-o", tmp]
+# per-source extra hipcc flags (none at present)
+FILE_FLAGS = {}
+OBJ_DIR = os.path.join(HERE, "_build")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
+        raise RuntimeError(f"hipcc failed with exit code {r.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source to an object (in parallel), then link libffd.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in srcs:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        jobs.append((obj, [hipcc(), *compile_flags, *FILE_FLAGS.get(os.path.basename(src), []), *inc, "-c", src,
+                           "-o", obj]))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for _, cmd in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
