@@ -408,6 +408,54 @@ def measure_dense(w, steps, warmup, d, torch, sm_scale, flush):
             "read_between_visits": (R - 1) * byts}
 
 
+def measure_split(w, delta, steps, warmup, c, d, torch, sm_scale, flush):
+    """The split path of the same step (debug split_mode 2: a scan kernel that
+    writes keep bitmaps, then a refine kernel over the compacted kept blocks):
+    whole step, scan kernel alone and refine kernel alone, each a graph of
+    `steps` launches over rotated copies, with their algorithmic bytes (48 B
+    per token-head scanned; 440 B per kept token-head refined: residual 128 +
+    rscale 8 + V 256 + the thumbnail read again, 48)."""
+    import sparse_long_context_ffd_amd as ffd
+    shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
+    base = ffd.PackedCache(shape)
+    ffd.quantize_k(shape, d["k"], 0, w.max_len, base)
+    ffd.pack_v(shape, d["v"], 0, w.max_len, base)
+    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+    nb = w.max_len // 64
+    keep = torch.zeros((w.batch, w.kv_heads, nb), dtype=torch.uint8, device="cuda")
+    ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, out, ws,
+                    debug={"keep": keep, "split_mode": 2, "pm_mode": 1})
+    torch.cuda.synchronize()
+    keep = keep.cpu().numpy().astype(bool)
+    lens = c["seq_lens"].astype(np.int64)
+    tok_total = int(lens.sum()) * w.kv_heads
+    kept_tok = sum(int(np.repeat(keep[b, :, :(int(L) + 63) // 64], 64, axis=1)[:, :int(L)].sum())
+                   for b, L in enumerate(lens))
+    scan_bytes, refine_bytes = SCAN_BYTES * tok_total, (REFINE_BYTES + SCAN_BYTES) * kept_tok
+    layer_bytes = sum(n for n in ffd.cache_bytes(shape).values())
+    R = copies_for(scan_bytes + refine_bytes, layer_bytes)
+    layers = [base] + [base.clone() for _ in range(R - 1)]
+
+    def step(i, stages=0):
+        ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, out, ws,
+                        debug={"split_mode": 2, "pm_mode": 1, "stages": stages})
+
+    step(0)
+    res = {}
+    for name, st in (("step", 0), ("scan", 8), ("refine", 16)):
+        g = graph_of([lambda i=i: step(i, st) for i in range(steps)], torch)
+        g.replay()
+        res[name] = timed_replay(g, torch, flush) * 1e3 / steps
+        del g
+    del layers, base
+    rf = lambda byts, us: {"achieved": round(byts / (us * 1e3), 1), "frac": round(byts / (us * 1e3) / HBM_PEAK_GBPS, 4),
+                           "bytes_per_launch": byts, "kernel_us": round(us, 3)}
+    return {"us_per_step": round(res["step"], 3), "scan_kernel": rf(scan_bytes, res["scan"]),
+            "refine_kernel": rf(refine_bytes, res["refine"]), "layers_rotated": R,
+            "note": "debug split_mode 2 (not the default path: slower than the fused kernel here)"}
+
+
 def roofline_of(r, workload):
     """The attend kernel's roofline entry of one measure_ffd result."""
     ach = r["attend_bytes"] / (r["attend_us_mean"] * 1e3)
@@ -416,7 +464,7 @@ def roofline_of(r, workload):
             "bytes_per_launch": r["attend_bytes"], "attend_kernel_us": round(r["attend_us_mean"], 3)}
 
 
-def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True, scan_only=False):
+def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True, scan_only=False, split=False):
     """One workload beside the headline: FFD step and attend kernel (roofline),
     the dense baseline, and optionally the scan-only variant (delta = -1e30)."""
     c, d = prepare(w, seed, torch)
@@ -433,6 +481,8 @@ def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True,
         out["scan_only"] = {"delta": -1e30, "keep_fraction": round(so["keep_fraction"], 5),
                             "us_per_step": round(so["us_per_step"], 3), "roofline_attend": roofline_of(so, None),
                             "layers_rotated": so["layers_rotated"]}
+    if split:
+        out["split_path"] = measure_split(w, delta, steps, warmup, c, d, torch, sm_scale, flush)
     if dense:
         dn = measure_dense(w, max(10, steps // 2), min(warmup, 5), d, torch, sm_scale, flush)
         out.update({"dense_us_per_step": round(dn["us_per_step"], 3), "dense_gbps": round(dn["gbps"], 1),
@@ -593,7 +643,8 @@ def main():
     warm_leg = min(args.warmup, 10)
     if "long" in legs:
         result["long_context"] = leg("long_context", WORKLOADS["long_256k"], WORKLOADS["long_256k"].deltas[0],
-                                     steps_leg, warm_leg, args.seed, torch, sm_scale, flush, scan_only=True)
+                                     steps_leg, warm_leg, args.seed, torch, sm_scale, flush, scan_only=True,
+                                     split=True)
     if "qwen" in legs:
         wq = WORKLOADS["qwen7b_b16_16k32k"]
         result["batched_qwen"] = leg("batched_qwen", wq, wq.deltas[0], steps_leg, warm_leg, args.seed, torch,

@@ -128,7 +128,8 @@ typedef struct ffd_cache {
  *  attend_start  hipEvent_t recorded on the stream right before the fused
  *  attend_stop   scan + refine kernel, and right after it
  *  stages        0 = the whole step; otherwise a bitmask of the launches to
- *                enqueue (1 = pseudo-max, 2 = scan + refine, 4 = merge).  A
+ *                enqueue (1 = pseudo-max, 2 = scan + refine, 4 = merge; see
+ *                split_mode for 8 and 16).  A
  *                partial call reuses what the previous call left in the same
  *                workspace (for timing one kernel alone).  When the
  *                pseudo-max runs inside the scan + refine launch (pm_mode),
@@ -141,7 +142,22 @@ typedef struct ffd_cache {
  *                3 = inside it, but every chunk computes the pseudo-max itself
  *                (the path of a workspace's first call).  2 and 3 need the
  *                union selection, no run-time termination and stages 0 or both
- *                2 and 4, else FFD_ERR_ARG.                                  */
+ *                2 and 4, else FFD_ERR_ARG.
+ *  split_mode    how stages 2 and 3 run for the union selection without
+ *                run-time termination: as the one fused scan + refine kernel,
+ *                or split into two kernels -- a scan that writes one keep
+ *                bitmap word per 32 blocks, and a refine over the compacted
+ *                kept blocks only, cut into equal units spread over the
+ *                device.  0 = the library's choice (ffd_plan_split: at
+ *                present the fused kernel everywhere, the faster one on the
+ *                shapes measured); 1 = the fused kernel; 2 = the two kernels
+ *                (needs the pseudo-max in its own launch, at most 1024
+ *                (sequence, KV head) pairs and 8192 bitmap words, else
+ *                FFD_ERR_ARG).  On the
+ *                split path stages bit 8 enqueues the scan alone and bit 16
+ *                the refine alone (bit 2 both); elsewhere bits 8 and 16 are
+ *                FFD_ERR_ARG.  The kept blocks are the same on both paths; the
+ *                outputs differ only in summation order.                      */
 typedef struct ffd_debug {
   float* m_tilde;
   float* bmax;
@@ -151,6 +167,7 @@ typedef struct ffd_debug {
   int32_t stages;
   uint8_t* tmask;
   int32_t pm_mode;
+  int32_t split_mode;
 } ffd_debug_t;
 
 /* What each query head attends inside the blocks kept for its KV head (the
@@ -189,6 +206,11 @@ int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
  * heads); otherwise about 1380 work-groups per launch, at most 4 blocks each
  * on short caches.  ffd_dense_decode_attn aims at about 2048 instead. */
 int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks);
+
+/* Whether a whole ffd_decode_attn step (union selection, no debug) for
+ * `shape` runs stages 2 and 3 as the split scan + refine kernels (split = 1)
+ * or as the fused kernel (0); see ffd_debug_t.split_mode (host call). */
+int ffd_plan_split(const ffd_shape_t* shape, int32_t* split);
 
 /* Where the pseudo-max of a whole ffd_decode_attn step (union selection, no
  * debug) runs for `shape` (host call): n_parts = support blocks per sequence

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     pack_v,
     plan,
     plan_pseudomax,
+    plan_split,
     quantize_k,
     strerror,
     stream_read,
@@ -28,6 +29,6 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "EXPORTED", "FFDError", "LIB_PATH", "PackedCache", "Shape", "append_kv", "cache_bytes", "decode_attn", "decode_attn_noalloc",
-    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "quantize_k", "strerror", "stream_read", "workspace_bytes",
+    "dense_decode_attn", "lib", "make_shape", "pack_v", "plan", "plan_pseudomax", "plan_split", "quantize_k", "strerror", "stream_read", "workspace_bytes",
     "workspace_bytes_ex",
 ]

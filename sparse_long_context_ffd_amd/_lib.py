@@ -20,7 +20,7 @@ STATUS = {
     -5: "FFD_ERR_WORKSPACE", -6: "FFD_ERR_ARG", -7: "FFD_ERR_HIP", -8: "FFD_ERR_TOO_LARGE",
 }
 EXPORTED = (
-    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_workspace_bytes_ex", "ffd_plan", "ffd_plan_pseudomax", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
+    "ffd_cache_bytes", "ffd_workspace_bytes", "ffd_workspace_bytes_ex", "ffd_plan", "ffd_plan_pseudomax", "ffd_plan_split", "ffd_quantize_k", "ffd_pack_v", "ffd_append_kv",
     "ffd_decode_attn", "ffd_decode_attn_select", "ffd_decode_attn_ex", "ffd_decode_attn_noalloc",
     "ffd_dense_decode_attn", "ffd_stream_read", "ffd_strerror", "ffd_version",
 )
@@ -48,7 +48,7 @@ class Cache(ctypes.Structure):
 class Debug(ctypes.Structure):
     _fields_ = [("m_tilde", ctypes.c_void_p), ("bmax", ctypes.c_void_p), ("keep", ctypes.c_void_p),
                 ("attend_start", ctypes.c_void_p), ("attend_stop", ctypes.c_void_p), ("stages", ctypes.c_int32),
-                ("tmask", ctypes.c_void_p), ("pm_mode", ctypes.c_int32)]
+                ("tmask", ctypes.c_void_p), ("pm_mode", ctypes.c_int32), ("split_mode", ctypes.c_int32)]
 
 SELECTIONS = {"union": 0, "head_block": 1, "head_token": 2}
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.ffd_workspace_bytes_ex.argtypes = [P(Shape), P(DecodeOpts), P(SZ)]
         L.ffd_plan.argtypes = [P(Shape), P(I32), P(I32)]
         L.ffd_plan_pseudomax.argtypes = [P(Shape), P(I32), P(I32)]
+        L.ffd_plan_split.argtypes = [P(Shape), P(I32)]
         L.ffd_quantize_k.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_pack_v.argtypes = [P(Shape), V, I32, I32, P(Cache), V]
         L.ffd_append_kv.argtypes = [P(Shape), V, V, V, P(Cache), V]
@@ -160,6 +161,14 @@ def plan_pseudomax(shape: Shape) -> Tuple[int, bool]:
     n, g = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().ffd_plan_pseudomax(ctypes.byref(shape), ctypes.byref(n), ctypes.byref(g)), "ffd_plan_pseudomax")
     return n.value, bool(g.value)
+
+
+def plan_split(shape: Shape) -> bool:
+    """Whether a whole union step runs stages 2 and 3 as the split scan +
+    refine kernels (ffd_plan_split)."""
+    n = ctypes.c_int32()
+    _check(lib().ffd_plan_split(ctypes.byref(shape), ctypes.byref(n)), "ffd_plan_split")
+    return bool(n.value)
 
 
 # ---------------------------------------------------------------- tensor plumbing
@@ -261,7 +270,7 @@ def decode_attn(shape: Shape, q, cache: PackedCache, seq_lens, delta: float, sm_
     if debug is not None:
         dbg = Debug(_ptr(debug.get("m_tilde")), _ptr(debug.get("bmax")), _ptr(debug.get("keep")),
                     debug.get("attend_start"), debug.get("attend_stop"), int(debug.get("stages", 0)),
-                    _ptr(debug.get("tmask")), int(debug.get("pm_mode", 0)))
+                    _ptr(debug.get("tmask")), int(debug.get("pm_mode", 0)), int(debug.get("split_mode", 0)))
     if art is not None:
         opts = _opts(select, art)
         _check(lib().ffd_decode_attn_ex(ctypes.byref(shape), _ptr(q), ctypes.byref(c), _ptr(seq_lens),

@@ -53,9 +53,18 @@ int check_shape(const ffd_shape_t* s) {
   return FFD_OK;
 }
 
+// Split path (long caches): refine work-groups at most (the workspace holds a
+// partial slot per refine unit: at most this many plus one per (sequence, KV
+// head)), and bitmap words the refine keeps in LDS at most.
+constexpr int kRefineGroupsMax = 2048;
+constexpr long long kSplitMaxWords = 8192;
+constexpr long long kSplitMaxHeads = 1024;  // (sequence, KV head) pairs: unit starts and counts in LDS
+
 struct Plan {
-  int nblk_cap, cb, nchunk, npart;
-  size_t sync_off, pmw_off, pmax_off, ml_off, o_off, total;
+  int nblk_cap, cb, nchunk, npart, nword_cap;
+  size_t sync_off, pmw_off, pmax_off, ml_off, o_off;
+  size_t km_off, us_off, sml_off, so_off;  // split path: bitmap words, unit starts, unit partials
+  size_t total;
 };
 
 // Work split: one work-group per chunk of cb blocks (4 waves, one 16-token tile
@@ -102,7 +111,17 @@ Plan make_plan(const ffd_shape_t* s, long long target = kTargetGroups, int fixed
   p.pmax_off = p.pmw_off + round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(uint64_t), kAlign);
   p.ml_off = p.pmax_off + round_up((size_t)s->batch * p.npart * s->num_q_heads * sizeof(float), kAlign);
   p.o_off = p.ml_off + round_up(rows * p.nchunk * 2 * sizeof(float), kAlign);
-  p.total = p.o_off + round_up(rows * p.nchunk * 128 * sizeof(float), kAlign);
+  const size_t fused_end = p.o_off + round_up(rows * p.nchunk * 128 * sizeof(float), kAlign);
+  // the split path's arrays reuse the space of the fused path's partials
+  const size_t heads = (size_t)s->batch * s->num_kv_heads;
+  const size_t slots = ((size_t)kRefineGroupsMax + heads) * (s->num_q_heads / s->num_kv_heads);
+  p.nword_cap = (p.nblk_cap + 31) / 32;
+  p.km_off = p.ml_off;
+  p.us_off = p.km_off + round_up(heads * p.nword_cap * sizeof(uint32_t), kAlign);
+  p.sml_off = p.us_off + round_up((heads + 1) * sizeof(int32_t), kAlign);
+  p.so_off = p.sml_off + round_up(slots * 2 * sizeof(float), kAlign);
+  const size_t split_end = p.so_off + round_up(slots * 128 * sizeof(float), kAlign);
+  p.total = fused_end > split_end ? fused_end : split_end;
   return p;
 }
 
@@ -127,6 +146,40 @@ int art_stream_blocks(const ffd_shape_t* s, const ffd_decode_opts_t& o) {
 // the plan a decode call with options `o` runs
 Plan decode_plan(const ffd_shape_t* s, const ffd_decode_opts_t& o) {
   return o.art_patience > 0 ? make_plan(s, kTargetGroups, art_stream_blocks(s, o)) : make_plan(s);
+}
+
+// The split scan + refine kernels run a union step whose pseudo-max has its
+// own launch when the refine's bitmap words fit its LDS.  They are not the
+// default anywhere: measured on MI355X they are slower than the fused kernel
+// at every benchmark shape (256K: scan 21.4 us + refine 42.9 us against 57.9
+// us fused; the batched Qwen-like and stress shapes keep nearly every block,
+// where re-reading their thumbnail costs more), so a whole step chooses them
+// only when debug->split_mode asks.
+bool split_possible(const ffd_shape_t* s, const Plan& pl) {
+  const long long heads = (long long)s->batch * s->num_kv_heads;
+  return heads <= kSplitMaxHeads && heads * pl.nword_cap <= kSplitMaxWords;
+}
+bool split_default(const ffd_shape_t*, const Plan&) { return false; }
+
+// Work-groups of the refine kernel: as many as are resident at once on the
+// current device (compute units x 2: the kernel runs at 2 waves per SIMD), at
+// most kRefineGroupsMax.  The compute-unit count is queried once per device.
+constexpr int kMaxDevicesCu = 64;
+std::atomic<int> g_cu_count[kMaxDevicesCu];
+
+int refine_groups(int G, int* groups) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesCu) return FFD_ERR_HIP;
+  int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return FFD_ERR_HIP;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
+  (void)G;
+  const int n = cus * 2;
+  *groups = n < kRefineGroupsMax ? n : kRefineGroupsMax;
+  return FFD_OK;
 }
 
 }  // namespace
@@ -195,6 +248,14 @@ int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks)
   const Plan p = make_plan(shape);
   *chunk_blocks = p.cb;
   *n_chunks = p.nchunk;
+  return FFD_OK;
+}
+
+int ffd_plan_split(const ffd_shape_t* shape, int32_t* split) {
+  const int st = check_shape(shape);
+  if (st) return st;
+  if (!split) return FFD_ERR_NULL;
+  *split = split_default(shape, make_plan(shape)) ? 1 : 0;
   return FFD_OK;
 }
 
@@ -359,9 +420,12 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
   p.pm_words = reinterpret_cast<unsigned long long*>(ws + pl.pmw_off);
   p.pm_sync = reinterpret_cast<unsigned long long*>(ws + pl.sync_off);
   int pm_mode = 0;
+  int split_mode = 0;
   if (debug) {
-    if (debug->stages < 0 || debug->stages > 7) return FFD_ERR_ARG;
+    if (debug->stages < 0 || debug->stages > 31) return FFD_ERR_ARG;
     if (debug->pm_mode < 0 || debug->pm_mode > 3) return FFD_ERR_ARG;
+    if (debug->split_mode < 0 || debug->split_mode > 2) return FFD_ERR_ARG;
+    split_mode = debug->split_mode;
     pm_mode = debug->pm_mode;
     p.stages = debug->stages;
     p.dbg_mt = debug->m_tilde;
@@ -402,6 +466,24 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
   p.pm_local = pm_mode == 3;
   p.pm_magic = ffd::kPmMagic ^ ((unsigned long long)shape->batch << 40) ^ ((unsigned long long)shape->num_q_heads << 24) ^
                ((unsigned long long)pl.npart << 4);
+  // Split path: the union selection without run-time termination, with the
+  // pseudo-max in its own launch; chosen by default on long caches
+  // (split_default), forced on or off by debug->split_mode 2 / 1.
+  const bool split_ok = selection == FFD_SELECT_UNION && o.art_patience == 0 && !p.pm_in_grid &&
+                        split_possible(shape, pl);
+  if (split_mode == 2 && !split_ok) return FFD_ERR_ARG;
+  if ((p.stages & 24) && !(split_mode == 2 || (split_mode == 0 && split_ok && split_default(shape, pl))))
+    return FFD_ERR_ARG;  // the scan / refine stage bits exist on the split path only
+  p.split = split_mode == 2 || (split_mode == 0 && split_ok && split_default(shape, pl));
+  p.nword_cap = pl.nword_cap;
+  if (p.split) {
+    const int rg = refine_groups(shape->num_q_heads / shape->num_kv_heads, &p.refine_groups);
+    if (rg) return rg;
+    p.kmask = reinterpret_cast<uint32_t*>(ws + pl.km_off);
+    p.unit_start = reinterpret_cast<int*>(ws + pl.us_off);
+    p.part_ml = reinterpret_cast<float2*>(ws + pl.sml_off);
+    p.part_o = reinterpret_cast<float*>(ws + pl.so_off);
+  }
   return from_hip(ffd::launch_ffd_decode(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -41,7 +41,8 @@ struct DecodeParams {
   uint16_t* out;           // [B][Hq][128] fp16
   hipEvent_t ev_start;     // optional, recorded around the attend kernel
   hipEvent_t ev_stop;
-  int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge
+  int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge (split path:
+                           // bit 3 the scan kernel alone, bit 4 the refine kernel alone)
   int select;              // kSelectUnion / kSelectHeadBlock / kSelectHeadToken
   int art_patience;        // run-time termination: stable steps before a chunk stops (0 = off)
   float art_tau, art_phi;  // ... thresholds on the probe's norm change and 1 - cosine
@@ -49,6 +50,13 @@ struct DecodeParams {
   int pm_in_grid;          // 1: pseudo-max work-groups lead the attend grid (no separate launch)
   int pm_local;            // 1: every chunk computes the pseudo-max itself (tests the fallback)
   unsigned long long pm_magic;  // kPmMagic keyed to the word layout (written by the merge, checked by chunks)
+  // split path (long caches): scan kernel -> keep bitmap words, refine kernel
+  // over the compacted kept blocks -> per-unit partials [slot][G] (o, m, l)
+  int split;               // 1: scan + refine kernels instead of the fused attend kernel
+  uint32_t* kmask;         // [B * Hkv][nword_cap] keep bitmap words (bit j: block 32 * word + j)
+  int* unit_start;         // [B * Hkv + 1] first refine unit of each (sequence, KV head)
+  int nword_cap;           // ceil(nblk_cap / 32)
+  int refine_groups;       // refine work-groups
   int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
   float delta, sm_scale;
 };
@@ -60,6 +68,8 @@ hipError_t launch_pack_v(const void* v, int B, int Hkv, int L_cap, int t_begin, 
 hipError_t launch_append(const void* k_new, const void* v_new, const int32_t* pos, int B, int Hkv, int L_cap,
                          void* codes, void* sz, void* res, void* rsc, void* vt, hipStream_t stream);
 hipError_t launch_ffd_decode(const DecodeParams& p, hipStream_t s);
+// split path: which = 1 scan, 2 refine, 3 both
+hipError_t launch_split(const DecodeParams& p, hipStream_t s, int which);
 hipError_t launch_dense_decode(const DecodeParams& p, hipStream_t s);
 // streaming-read probe over kStreamReadGroups work-groups; sink holds one
 // 32-bit XOR per work-group

@@ -68,7 +68,7 @@ def cache_to_host(cache):
     return {f: getattr(cache, f).cpu().numpy() for f in ("codes", "sz", "res", "rscale", "v")}
 
 
-def _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, pm_mode):
+def _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, pm_mode, split_mode=0):
     import sparse_long_context_ffd_amd as ffd
     B, Hq, Hkv = shape.batch, shape.num_q_heads, shape.num_kv_heads
     nb = shape.max_seq_len // 64
@@ -79,20 +79,22 @@ def _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, sele
         "keep": torch.full((B, Hkv, nb), 7, dtype=torch.uint8, device="cuda"),
         "tmask": torch.full((B, Hq, shape.max_seq_len), 7, dtype=torch.uint8, device="cuda"),
     }
-    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws, debug={**dbg, "pm_mode": pm_mode},
-                    select=select, art=art)
+    ffd.decode_attn(shape, q_dev, cache, lens_dev, delta, sm_scale, out, ws,
+                    debug={**dbg, "pm_mode": pm_mode, "split_mode": split_mode}, select=select, art=art)
     torch.cuda.synchronize()
     return {"out": out.float().cpu().numpy(), **{k: v.cpu().numpy() for k, v in dbg.items()}}
 
 
-# the pseudo-max paths one decode is run through (debug pm_mode, in order, on
-# one workspace zeroed before the first): inside the attend launch on the
-# fresh workspace (no initialised sync words, so every chunk computes the
-# pseudo-max itself), inside it again (the chunks read the words the leading
-# work-groups publish), the separate launch, and inside it with every chunk
-# forced to compute it.  Selection variants and run-time termination have the
-# separate launch only.
+# the pseudo-max paths one decode is run through with the fused scan + refine
+# kernel (debug pm_mode, in order, on one workspace zeroed before the first):
+# inside the attend launch on the fresh workspace (no initialised sync words,
+# so every chunk computes the pseudo-max itself), inside it again (the chunks
+# read the words the leading work-groups publish), the separate launch, and
+# inside it with every chunk forced to compute it.  Selection variants and
+# run-time termination have the separate launch only.  A union step also runs
+# the split scan + refine kernels (SPLIT: separate pseudo-max launch).
 PM_PATHS = (2, 2, 1, 3)
+SPLIT = (1, 2)
 
 
 def ws_bytes(shape, select="union", art=None):
@@ -133,16 +135,26 @@ def gpu_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale=SM_SCALE, w
         prod = production_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, select=select, art=art)
         assert np.array_equal(prod, got["out"]), f"production call ({select}, art={art}) differs from the debug run"
         return got
-    runs = [_decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, mode)
+    runs = [_decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, mode, 1)
             for mode in PM_PATHS]
     for mode, r in zip(PM_PATHS[1:], runs[1:]):
         for k, v in runs[0].items():
             assert np.array_equal(v, r[k], equal_nan=True), f"pseudo-max path (pm_mode {mode}) changed {k}"
+    # the split scan + refine kernels: the same decisions and diagnostics bit
+    # for bit (same arithmetic); the output differs only in summation order and
+    # is held to the oracle separately (check_head, "out_split")
+    sp = _decode_once(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws, select, art, *SPLIT)
+    for k in ("m_tilde", "bmax", "keep", "tmask"):
+        assert np.array_equal(sp[k], runs[1][k], equal_nan=True), f"split path changed {k}"
+    got = dict(runs[1], out_split=sp["out"])
+    split_default = ffd.plan_split(shape)
     pws = torch.full((ffd.workspace_bytes(shape),), 0x5A, dtype=torch.uint8, device="cuda")
     for i in range(2):
         prod = production_decode(shape, q_dev, cache, lens_dev, delta, torch, sm_scale, ws=pws)
-        assert np.array_equal(prod, runs[1]["out"]), f"production call {i} differs from the debug run"
-    return runs[1]
+        ref = sp["out"] if split_default else runs[1]["out"]
+        assert np.array_equal(prod, ref), \
+            f"production call {i} differs from the debug run of its path (split={split_default})"
+    return got
 
 
 def gpu_dense(shape, q_dev, k_dev, v_dev, lens_dev, torch, sm_scale=SM_SCALE, ws=None):
@@ -207,12 +219,15 @@ def check_head(orc, q16, pk_head, V16, L, delta, got, b, h, G, sink=64, local=25
         assert bad.size == 0, f"{label} {select}: token decisions differ at (head, token) {bad[:8].tolist()}"
         tmask = (tm == 1) & tok[None, :]
     ref = orc.decode_head(q16, pk_head, V16, L, delta, sm_scale, sink, local, keep=keep, tmask=tmask)["out"]
-    g_out = got["out"][b, h * G:(h + 1) * G]
-    d = g_out - ref
-    max_abs = float(np.abs(d).max())
-    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
-    rmse = float(np.sqrt(np.mean(d * d)))
-    assert max_abs <= ATOL and rel <= RTOL_L2, f"{label} output max-abs {max_abs} rel-L2 {rel}"
+    for key in ("out", "out_split"):
+        if key not in got:
+            continue
+        d = got[key][b, h * G:(h + 1) * G] - ref
+        ma = float(np.abs(d).max())
+        rl = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30))
+        assert ma <= ATOL and rl <= RTOL_L2, f"{label} {key} max-abs {ma} rel-L2 {rl}"
+        if key == "out":
+            max_abs, rel, rmse = ma, rl, float(np.sqrt(np.mean(d * d)))
     return {"keep_frac": float(keep.mean()), "exempt": int(nb - pk.sum() - pd.sum()),
             "mt_err": mt_err, "bmax_err": bm_err, "max_abs": max_abs, "rel_l2": rel, "rmse": rmse,
             "mask_equal": bool((keep == o["keep"]).all()),

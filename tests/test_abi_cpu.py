@@ -102,12 +102,12 @@ def test_debug_argument_errors():
     s = ffd.make_shape(1, 32, 8, 16384)
     c = _lib.Cache(FAKE, FAKE, FAKE, FAKE, FAKE)
 
-    def dec(stages, pm_mode, shape=s, selection=0, art=0):
-        d = _lib.Debug(None, None, None, None, None, stages, None, pm_mode)
+    def dec(stages, pm_mode, shape=s, selection=0, art=0, split_mode=0):
+        d = _lib.Debug(None, None, None, None, None, stages, None, pm_mode, split_mode)
         o = _lib.DecodeOpts(selection, art, 0.1, 0.1)
         return ffd.lib().ffd_decode_attn_ex(ctypes.byref(shape), FAKE, ctypes.byref(c), FAKE, 5.0, 0.088,
                                             ctypes.byref(o), FAKE, FAKE, _ws(shape), ctypes.byref(d), None)
-    assert dec(8, 0) == -6 and dec(-1, 0) == -6
+    assert dec(32, 0) == -6 and dec(-1, 0) == -6
     assert dec(0, 4) == -6 and dec(0, -1) == -6
     # the pseudo-max inside the attend launch needs the merge in the same call,
     for mode in (2, 3):
@@ -119,6 +119,20 @@ def test_debug_argument_errors():
         # and the support words of a work-group (npart * G <= 256)
         big = ffd.make_shape(1, 8, 1, 1 << 20, local=(1 << 20) - 64)
         assert dec(0, mode, shape=big) == -6
+    # split path: modes 0..2; forcing it needs the union selection, no run-time
+    # termination and the pseudo-max in its own launch; the scan / refine stage
+    # bits exist on it only (16K runs fused by default, 256K split)
+    assert dec(0, 1, split_mode=3) == -6 and dec(0, 1, split_mode=-1) == -6
+    assert dec(0, 2, split_mode=2) == -6 and dec(0, 3, split_mode=2) == -6
+    assert dec(0, 1, split_mode=2, selection=1) == -6 and dec(0, 1, split_mode=2, art=2) == -6
+    for st in (8, 16, 24):
+        assert dec(st, 0) == -6 and dec(st, 1, split_mode=1) == -6
+    long_ = ffd.make_shape(1, 32, 8, 262144)
+    assert not ffd.plan_split(s) and not ffd.plan_split(long_)  # the fused kernel is the default
+    assert dec(8, 0, shape=long_, split_mode=1) == -6 and dec(16, 0, shape=long_) == -6
+    # too many bitmap words for the refine's LDS: no split path
+    wide = ffd.make_shape(64, 64, 8, 262144)
+    assert dec(0, 1, shape=wide, split_mode=2) == -6
 
 
 def _decode_sel(shape, selection, q=FAKE, ws=FAKE):
@@ -167,19 +181,22 @@ def test_art_stream_length_and_workspace():
                                                 ctypes.byref(n)) == -6
     for sh, good in ((s4, 32), (s4, 1), (s8, 16), (s8, 0)):
         assert _decode_ex(sh, O(0, 1, 0.1, 0.1, good), q=None) == -1
-    # partials: one per stream of 4-block chunks; the default length fits ffd_workspace_bytes
-    rows, nblk = 32, 16384 // 64
+    # partials: one per stream; the default length fits ffd_workspace_bytes, a
+    # 1-block stream on a 256K cache needs more
     assert ffd.workspace_bytes_ex(s4, art=(0.1, 0.1, 1)) <= ffd.workspace_bytes(s4)
-    one = ffd.workspace_bytes_ex(s4, art=(0.1, 0.1, 1, 1))
-    assert one >= rows * nblk * (128 + 2) * 4 > ffd.workspace_bytes(s4)
+    s4l = ffd.make_shape(1, 32, 8, 262144)
+    rows, nblk = 32, 262144 // 64
+    assert ffd.workspace_bytes_ex(s4l, art=(0.1, 0.1, 1)) <= ffd.workspace_bytes(s4l)
+    one = ffd.workspace_bytes_ex(s4l, art=(0.1, 0.1, 1, 1))
+    assert one >= rows * nblk * (128 + 2) * 4 > ffd.workspace_bytes(s4l)
     # the stream length is ignored without termination; opts NULL = the plain step
     assert ffd.workspace_bytes_ex(s4) == ffd.workspace_bytes_ex(s4, art=None)
     n = ctypes.c_size_t()
     assert ffd.lib().ffd_workspace_bytes_ex(ctypes.byref(s4), None, ctypes.byref(n)) == 0
     assert n.value == ffd.workspace_bytes_ex(s4) <= ffd.workspace_bytes(s4)
     # a call with a too-small workspace for its stream length is refused
-    assert _decode_ex(s4, O(0, 1, 0.1, 0.1, 1), wsb=ffd.workspace_bytes(s4)) == -5
-    assert _decode_ex(s4, O(0, 1, 0.1, 0.1, 1), q=None, wsb=one) == -1
+    assert _decode_ex(s4l, O(0, 1, 0.1, 0.1, 1), wsb=ffd.workspace_bytes(s4l)) == -5
+    assert _decode_ex(s4l, O(0, 1, 0.1, 0.1, 1), q=None, wsb=one) == -1
 
 
 def test_dense_and_pack_argument_errors():
@@ -240,18 +257,27 @@ def test_cache_and_workspace_sizes():
     # sync words (16 B), in-grid pseudo-max words (8 B), separate-launch maxima
     # (4 B), chunk (m, l) and o partials; each region 256-byte aligned
     need = 16 + rows * npart * 8 + rows * npart * 4 + rows * nch * 8 + rows * nch * 128 * 4
-    assert need <= ffd.workspace_bytes(s) <= need + 5 * 256
+    # the split path instead: keep bitmap words, unit starts, and a partial per
+    # refine unit and query head of the group (at most 2048 + B*Hkv units)
+    heads, G = 2 * 4, 7
+    need_split = (16 + rows * npart * 8 + rows * npart * 4 + heads * math.ceil(512 / 32) * 4 + (heads + 1) * 4
+                  + (2048 + heads) * G * (8 + 128 * 4))
+    need = max(need, need_split)
+    assert need <= ffd.workspace_bytes(s) <= need + 8 * 256
 
 
-def test_workspace_covers_the_dense_split():
-    # at 256K the decode splits into 24-block chunks, the dense baseline into
-    # 16-block ones: the workspace holds the larger set of partials
+def test_workspace_covers_the_dense_and_split_paths():
+    # at 256K the fused decode splits into 24-block chunks, the dense baseline
+    # into 16-block ones, the split path into refine units: the workspace holds
+    # the largest set of partials
     s = ffd.make_shape(1, 32, 8, 262144)
     assert ffd.plan(s)[0] == 24
-    rows, npart, nch_dense = 32, 6, 4096 // 16
-    need_dense = 16 + rows * npart * 8 + rows * npart * 4 + rows * nch_dense * (8 + 128 * 4)
-    assert ffd.workspace_bytes(s) >= need_dense
-    assert ffd.workspace_bytes(s) <= need_dense + 5 * 256
+    rows, npart, nch_dense, heads, G = 32, 6, 4096 // 16, 8, 4
+    head = 16 + rows * npart * 8 + rows * npart * 4
+    need_dense = head + rows * nch_dense * (8 + 128 * 4)
+    need_split = head + heads * (4096 // 32) * 4 + (heads + 1) * 4 + (2048 + heads) * G * (8 + 128 * 4)
+    need = max(need_dense, need_split)
+    assert need <= ffd.workspace_bytes(s) <= need + 8 * 256
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,in_grid", [(1, 32, 8, 16384, True), (1, 4, 1, 4096, True),
