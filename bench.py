@@ -73,16 +73,16 @@ TOUCH_BETWEEN_VISITS = 1.1e9  # bytes read between two visits of one rotated cac
 ROTATE_BUDGET = 48e9          # device bytes the rotated copies of one leg may take
 FLUSH_BYTES = 1 << 30         # the pre-replay copy: 1 GiB read + 1 GiB written
 # HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
-# `bench.py --workload W --no-long --no-cpu-baseline --steps 20 --warmup 5`
+# `bench.py --workload W --no-long --no-variants --no-cpu-baseline --steps 20 --warmup 5`
 # (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the dispatches of
 # the attend kernel the step runs).  Both counters are scaled by what they read for the plain
-# 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088 KiB
+# 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088.5 KiB
 # for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
 # while the kernel sources hash to the digest it was recorded with.
-FETCH_SCALE, WRITE_SCALE = 262144 / 131088.4, 1.0
+FETCH_SCALE, WRITE_SCALE = 262144 / 131088.5, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "5e6ca527002af4c5", "fetch": 10249.5, "write": 695.5},
-    "long_256k": {"sources": "5e6ca527002af4c5", "fetch": 136671.19, "write": 2463.66},
+    "llama8b_16k": {"sources": "406cbba61490a52e", "fetch": 10248.56, "write": 695.5},
+    "long_256k": {"sources": "406cbba61490a52e", "fetch": 136711.00, "write": 2464.47},
 }
 REPLAYS = 10  # replays of the K-step graph behind the reported spread (the first is the timed one)
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
