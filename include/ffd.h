@@ -341,8 +341,15 @@ int ffd_decode_attn_noalloc(const ffd_shape_t* shape, const void* q, const ffd_c
                             const int32_t* seq_lens, float delta, float sm_scale, void* out, void* stream);
 
 /* Dense flash-decode attention over fp16 K and V ([B][Hkv][max_seq_len][128]),
- * the speed baseline: out = softmax(q k^T * sm_scale) v over tokens [0, L).
- * Same argument rules as ffd_decode_attn. */
+ * the speed baseline.  The page's main results measure FFD's kernel and
+ * end-to-end speed against dense FlashAttention-2 decoding, which loads the
+ * whole fp16 KV cache every step (its problem statement: decode is bound by
+ * reloading the cache); this is that dense computation, as a split-KV
+ * flash-decode kernel of this library: out = softmax(q k^T * sm_scale) v over
+ * tokens [0, L), per query head h with KV head h / (Hq / Hkv).  K and V are in
+ * natural row-major order, 16-byte aligned, caller-owned; q, seq_lens, out,
+ * workspace and the error codes follow ffd_decode_attn (the workspace of
+ * ffd_workspace_bytes covers this call). */
 int ffd_dense_decode_attn(const ffd_shape_t* shape, const void* q, const void* k, const void* v,
                           const int32_t* seq_lens, float sm_scale, void* out, void* workspace,
                           size_t workspace_bytes, void* stream);
