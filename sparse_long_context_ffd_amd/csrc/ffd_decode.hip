@@ -78,9 +78,9 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
 //   phase B: every wave refines its tile of every kept block (residual, rscale
 //            and V of the next kept block loaded while the current one is
 //            computed), online softmax, P.V on MFMA
-// Dynamic LDS: per-block estimates [cb][4 waves][G][16], per-(block, wave, row
-// group) maxima [cb][16][G] (written only for the block-max diagnostic), the
-// combine area.
+// Dynamic LDS: per-block estimates [cb][4 waves][G][16], the combine area, and
+// (only when the block-max diagnostic is requested) per-(block, wave, row
+// group) maxima [cb][16][G].
 // ---------------------------------------------------------------------------
 // One leading work-group of the attend grid: support part `part` of (b, hkv),
 // published as the 64-bit word (epoch + 1) << 32 | fp32 bits per query head
@@ -119,7 +119,10 @@ struct AttendCfg {
   static constexpr int CBMAX = (G <= 4) ? 32 : 16;
   static constexpr size_t est_bytes(int cb) { return (size_t)cb * kWaves * G * 16 * sizeof(float); }
   static constexpr size_t tmax_bytes(int cb) { return (size_t)cb * 4 * kWaves * G * sizeof(float); }
-  static constexpr size_t lds_bytes(int cb) { return est_bytes(cb) + tmax_bytes(cb) + sizeof(CombineLds<G>); }
+  // the block-max diagnostic's area is allocated only when it is requested
+  static constexpr size_t lds_bytes(int cb, bool bmax) {
+    return est_bytes(cb) + sizeof(CombineLds<G>) + (bmax ? tmax_bytes(cb) : 0);
+  }
 };
 
 
@@ -225,10 +228,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
-  float* est = dyn;                                                // [cb][kWaves][G][16]
-  float* tmax = dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float);  // [cb][4*kWaves][G]
-  CombineLds<G>& cl =
-      *reinterpret_cast<CombineLds<G>*>(dyn + (AttendCfg<G>::est_bytes(cb) + AttendCfg<G>::tmax_bytes(cb)) / sizeof(float));
+  float* est = dyn;  // [cb][kWaves][G][16]
+  CombineLds<G>& cl = *reinterpret_cast<CombineLds<G>*>(dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float));
+  float* tmax = dyn + (AttendCfg<G>::est_bytes(cb) + sizeof(CombineLds<G>)) / sizeof(float);  // [cb][4*kWaves][G]
 
   const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
@@ -245,6 +247,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   if constexpr (!PMG) pm_s[tid] = pm_t;
   __syncthreads();  // q staged in LDS (and the partial maxima without PMG)
+  // Refine loads of a block: residual, its scales, V.
+  // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes).
+  // The residual and its scales load with the non-temporal hint (a wave's
+  // instruction covers whole lines); V keeps the default policy, since a
+  // lane's span is split over four loads and every line is read by four
+  // instructions in turn (with the hint, 25% slower).
+  const uint32_t v_lane = (uint32_t)(((4 * wave + ks) * kHeadDim + 8 * col) * 4 * sizeof(uint16_t));
+  const __amdgpu_buffer_rsrc_t r_res = make_rsrc(p.res + hb * kResBytes, nbc * kResBytes);
+  const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
+  const __amdgpu_buffer_rsrc_t r_v = make_rsrc(p.v + head * p.L_cap * kHeadDim, nbc * kVBytes);
+  auto load_block = [&](int j, RefineRegs& x) {
+    const uint32_t blk = (uint32_t)blk_of(j);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64<kNonTemporal>(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
+    x.S8 = buf_load_b64<kNonTemporal>(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
+  };
+  // Blocks always kept (sink and local window) are known before any threshold:
+  // the refine takes them first (the union selection without run-time
+  // termination, whose streams keep their order), and the first one's loads go
+  // out here, before the scan, so that its latency overlaps the scan and the
+  // decisions.
+  const int sink_end = p.sink > 0 ? ((min(p.sink, L) + 63) >> 6) : 0;
+  const int local_beg = p.local > 0 ? (max(0, L - p.local) >> 6) : nblk;
+  const uint64_t fmask = __builtin_amdgcn_ballot_w64(lane < nbl && (blk_of(lane) < sink_end || blk_of(lane) >= local_beg));
+  constexpr bool kForcedFirst = !ART;
+  RefineRegs X, Y;
+  if (kForcedFirst && fmask) load_block(__builtin_ctzll(fmask), X);
   typename QFrags<G>::Load ql;
   QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
@@ -460,8 +491,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
 
   // ---- block decisions (every wave derives the same mask) ----
   // forced blocks: [0, sink_end) and [local_beg, nblk)
-  const int sink_end = p.sink > 0 ? ((min(p.sink, L) + 63) >> 6) : 0;
-  const int local_beg = p.local > 0 ? (max(0, L - p.local) >> 6) : nblk;
   uint64_t kmask;
   {
     bool kp = false;
@@ -492,23 +521,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   MfmaSoftmax<NT> st;
   st.init();
   {
-    // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes).
-    // The residual and its scales load with the non-temporal hint (a wave's
-    // instruction covers whole lines); V keeps the default policy, since a
-    // lane's span is split over four loads and every line is read by four
-    // instructions in turn (with the hint, 25% slower).
-    const uint32_t v_lane = (uint32_t)(((4 * wave + ks) * kHeadDim + 8 * col) * 4 * sizeof(uint16_t));
-    const __amdgpu_buffer_rsrc_t r_res = make_rsrc(p.res + hb * kResBytes, nbc * kResBytes);
-    const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
-    const __amdgpu_buffer_rsrc_t r_v = make_rsrc(p.v + head * p.L_cap * kHeadDim, nbc * kVBytes);
-    auto load_block = [&](int j, RefineRegs& x) {
-      const uint32_t blk = (uint32_t)blk_of(j);
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64<kNonTemporal>(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
-      x.S8 = buf_load_b64<kNonTemporal>(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
-    };
     const float c2 = p.sm_scale * kLog2e, slack = 8.f / c2;
     // support tokens [0, sup_lo) and [sup_hi, L) (always attended per token)
     const int sup_lo = min(p.sink, L), sup_hi = max(0, L - p.local);
@@ -636,27 +648,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       ++art_step_no;
       return stop;
     };
-    // kept blocks in increasing order from the (wave-uniform) mask; the next
-    // one is loaded while the current one is computed, unconditionally as in
-    // the scan (the last block is re-read past the end of the mask)
-    uint64_t rem = kmask;
-    RefineRegs X, Y;
-    if (rem) load_block(__builtin_ctzll(rem), X);
-    while (rem) {
-      const int jx = __builtin_ctzll(rem);
-      rem &= rem - 1;
-      const int jy = rem ? __builtin_ctzll(rem) : jx;
-      load_block(jy, Y);
-      refine(jx, X);
-      if constexpr (ART)
-        if (art_stop()) break;
-      if (!rem) break;
-      rem &= rem - 1;
-      const int jn = rem ? __builtin_ctzll(rem) : jy;
-      load_block(jn, X);
-      refine(jy, Y);
-      if constexpr (ART)
-        if (art_stop()) break;
+    // kept blocks from the (wave-uniform) masks: the forced ones first, then
+    // the others, each in increasing order (under run-time termination all in
+    // increasing order).  The next block is loaded while the current one is
+    // computed, unconditionally as in the scan (the last block is re-read
+    // past the end of the list).
+    uint64_t rem_f = kForcedFirst ? (kmask & fmask) : 0ull, rem_o = kForcedFirst ? (kmask & ~fmask) : kmask;
+    auto pop = [&]() -> int {
+      if (rem_f) {
+        const int j = __builtin_ctzll(rem_f);
+        rem_f &= rem_f - 1;
+        return j;
+      }
+      if (rem_o) {
+        const int j = __builtin_ctzll(rem_o);
+        rem_o &= rem_o - 1;
+        return j;
+      }
+      return -1;
+    };
+    int jx = pop();
+    if (jx >= 0) {
+      if (!(kForcedFirst && fmask)) load_block(jx, X);  // (else loaded before the scan)
+      while (true) {
+        const int jy = pop();
+        load_block(jy >= 0 ? jy : jx, Y);
+        refine(jx, X);
+        if constexpr (ART)
+          if (art_stop()) break;
+        if (jy < 0) break;
+        const int jn = pop();
+        load_block(jn >= 0 ? jn : jy, X);
+        refine(jy, Y);
+        if constexpr (ART)
+          if (art_stop()) break;
+        if (jn < 0) break;
+        jx = jn;
+      }
     }
   }
   st.template store<G>(cl, wave, lane, p.sm_scale);
@@ -838,12 +866,76 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// The same merge for heads with at most 64 chunk partials (fused and dense
+// paths with nchunk <= 64): one wave per 32 output channels of a head, no
+// barriers, no LDS.  Lane c holds chunk c's (m, l) and computes its weight;
+// lane (channel j, half t) accumulates the chunk phases 4t .. 4t+3 (chunk
+// phase = c mod 8) of channel j, reading each chunk's weight with a lane read.
+// The association is merge_kernel's exactly (each phase in increasing chunk
+// order, the eight phases summed in order, the weight sum over the 64 lanes
+// by the same reduction), so both kernels give the same bits and the choice
+// between them never changes an output.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void merge64_kernel(DecodeParams p) {
+  const int lane = threadIdx.x;
+  if (p.pm_in_grid && blockIdx.x == 0 && lane == 0) {  // as in merge_kernel
+    const unsigned long long e = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.pm_sync + 1, (unsigned long long)((uint32_t)e + 1u), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.pm_sync, p.pm_magic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const size_t row = blockIdx.x >> 2;  // query head row; blockIdx.x & 3 = channel quarter
+  const int b = (int)(row / p.Hq), ch = 32 * (blockIdx.x & 3) + (lane & 31), half = lane >> 5;
+  const int nblk = (clamp_len(p, b) + 63) >> 6;
+  const int nch = p.interleaved ? min(p.nchunk, nblk) : (nblk + p.cb - 1) / p.cb;
+  // partial o of chunk c at byte c * 512 + 4 * channel; chunks past nch read
+  // as zero (bounds of the descriptor) and carry weight 0
+  const __amdgpu_buffer_rsrc_t r_o = make_rsrc(p.part_o + row * p.nchunk * kHeadDim, (uint32_t)nch * 512u);
+  const float2 v = lane < nch ? p.part_ml[row * p.nchunk + lane] : make_float2(-INFINITY, 0.f);
+  const uint32_t v_off = (uint32_t)ch * 4u + (uint32_t)half * 4u * 512u;  // + chunk (phase 4 * half)
+  float x[4][8];  // phase 4 * half + q, chunk 4 * half + q + 8 * i
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q][i] = __builtin_bit_cast(float, buf_load_b32(r_o, v_off, (uint32_t)(q + 8 * i) * 512u));
+  const bool live = v.y > 0.f;
+  const float M = wave_max(live ? v.x : -INFINITY);
+  const float w = live ? exp2f((v.x - M) * kLog2e) : 0.f;
+  const float ls = wave_sum(live ? w * v.y : 0.f);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float w0 = uniform_lane(w, q + 8 * i), w1 = uniform_lane(w, 4 + q + 8 * i);
+      const float wc = half ? w1 : w0;
+      acc[q] = wc > 0.f ? fmaf(wc, x[q][i], acc[q]) : acc[q];
+    }
+  // phases 0..3 (half 0), then 4..7 from the lane 32 places up
+  float o = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o += acc[q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o += __shfl_down(acc[q], 32, 64);
+  const float lsum = (ls + 0.f) + (0.f + 0.f);
+  if (half == 0) p.out[row * kHeadDim + ch] = __builtin_bit_cast(uint16_t, (_Float16)(o / lsum));
+}
+
+static void launch_merge(const DecodeParams& p, hipStream_t s) {
+  if (!p.split && p.nchunk <= 64 && 4ll * p.B * p.Hq < (1ll << 31))
+    hipLaunchKernelGGL(merge64_kernel, dim3((unsigned)(4ll * p.B * p.Hq)), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);
+}
+
+// ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
 template <int G, int SEL, bool ART, bool PMG>
 static void launch_attend(const DecodeParams& p, hipStream_t s) {
   const dim3 grid = PMG ? dim3((unsigned)((p.npart + p.nchunk) * p.Hkv * p.B)) : dim3(p.nchunk, p.Hkv, p.B);
-  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), grid, dim3(256), AttendCfg<G>::lds_bytes(p.cb), s, p);
+  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), grid, dim3(256), AttendCfg<G>::lds_bytes(p.cb, p.dbg_bmax != nullptr), s,
+                     p);
 }
 template <int G>
 static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
@@ -871,12 +963,12 @@ static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
       launch_attend<G, kSelectUnion, false, false>(p, s);
     if (p.ev_stop) (void)hipEventRecord(p.ev_stop, s);
   }
-  if (stages & 4) hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);
+  if (stages & 4) launch_merge(p, s);
 }
 template <int G>
 static void launch_dense_g(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL(dense_kernel<G>, dim3(p.nchunk, p.Hkv, p.B), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(merge_kernel, dim3(p.Hq, p.B, 4), dim3(256), 0, s, p);
+  launch_merge(p, s);
 }
 
 #define FFD_DISPATCH_G(FN, G_, P_, S_)    \

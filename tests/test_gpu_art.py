@@ -113,16 +113,18 @@ def test_art_group_sizes_and_ragged_batch():
 
 def test_art_streams_follow_the_call_not_the_batch_or_capacity():
     """The same sequences and queries visit the same blocks and give the same
-    output bits alone (batch 1), inside a batch of 16, and at two cache
+    output bits alone (batch 1), inside a batch of 16, and at three cache
     capacities: the streams come from the call's stream length, not from the
-    occupancy split of the launch."""
+    occupancy split of the launch.  The largest capacity has more than 64
+    streams per sequence, so its log-sum-exp merge runs in the general merge
+    kernel, the others in the 64-partial one: both must give the same bits."""
     import sparse_long_context_ffd_amd as ffd
     torch = torch_mod()
     G, Hkv, L, delta, art = 4, 2, 3000, 3.0, (0.05, 0.01, 1, 4)
     w1 = Workload("art_same_b1", 1, G * Hkv, Hkv, 3008, L, needles=4)
     c1 = make_case(w1, 7)
     runs = []
-    for B, L_cap, b0 in [(1, 3008, 0), (1, 8192, 0), (16, 4096, 9), (16, 8192, 2)]:
+    for B, L_cap, b0 in [(1, 3008, 0), (1, 8192, 0), (16, 4096, 9), (16, 8192, 2), (1, 32768, 0)]:
         rng = np.random.default_rng([B, L_cap])
         q = rng.standard_normal((B, G * Hkv, 128)).astype(np.float16)
         k = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
