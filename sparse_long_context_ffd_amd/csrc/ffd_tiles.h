@@ -471,15 +471,20 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 template <int NT>
 struct MfmaSoftmax {
   float m[NT], l[NT];  // running max and sum of the lane column's head
-  f4 o[NT][8];
+  // P.V accumulators.  One column tile (G <= 4): column 4h + g carries head h
+  // (four identical copies).  Two tiles (G > 4): one dense tile whose column c
+  // is head c, so each head is accumulated once (half the MFMAs and
+  // registers); its column equals the first copy of the one-tile layout bit
+  // for bit, since an MFMA computes every output column independently.
+  f4 o[1][8];
   __device__ void init() {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       m[n] = -INFINITY;
       l[n] = 0.f;
-#pragma unroll
-      for (int jm = 0; jm < 8; ++jm) o[n][jm] = f4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int jm = 0; jm < 8; ++jm) o[0][jm] = f4{0.f, 0.f, 0.f, 0.f};
   }
   // fold one tile.  x = raw dot products q.k of the lane's 4 rows per column
   // tile (rows past the sequence end -inf), c2 = sm_scale * log2(e), va = V^T
@@ -512,19 +517,37 @@ struct MfmaSoftmax {
       bhi[n] = h4{h01.x, h01.y, h23.x, h23.y};
       blo[n] = h4{l01.x, l01.y, l23.x, l23.y};
     }
+    h4 ph, pl;  // the B operand (weights) of the accumulator tile
+    float al;   // the rescale of the lane's accumulator column
+    if constexpr (NT == 1) {
+      ph = bhi[0];
+      pl = blo[0];
+      al = alpha[0];
+    } else {
+      // lane (column c, k-slice ks) takes head c's weights from lane
+      // (4 * (c mod 4), ks) of column tile c / 4; columns of no tile are zero
+      const int lane = __lane_id();
+      const int src = (((lane & 48) | ((lane & 3) << 2))) << 2, tile = (lane & 15) >> 2;
+      auto pick = [&](const h4 (&t)[NT], int k) {
+        const int v0 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int2, t[0])[k]);
+        const int v1 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int2, t[1])[k]);
+        return tile == 0 ? v0 : (tile == 1 ? v1 : 0);
+      };
+      ph = __builtin_bit_cast(h4, make_int2(pick(bhi, 0), pick(bhi, 1)));
+      pl = __builtin_bit_cast(h4, make_int2(pick(blo, 0), pick(blo, 1)));
+      const float a0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, alpha[0])));
+      const float a1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, alpha[1])));
+      al = tile == 0 ? a0 : (tile == 1 ? a1 : 1.f);
+    }
     if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int jm = 0; jm < 8; ++jm) o[n][jm] *= alpha[n];
+      for (int jm = 0; jm < 8; ++jm) o[0][jm] *= al;
     }
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int jm = 0; jm < 8; ++jm) {
-        o[n][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], bhi[n], o[n][jm], 0, 0, 0);
-        o[n][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], blo[n], o[n][jm], 0, 0, 0);
-      }
+    for (int jm = 0; jm < 8; ++jm) {
+      o[0][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], ph, o[0][jm], 0, 0, 0);
+      o[0][jm] = __builtin_amdgcn_mfma_f32_16x16x16f16(va[jm], pl, o[0][jm], 0, 0, 0);
+    }
   }
   // store the wave's state for the combine (m converted to a softmax logit):
   // lanes of group column 0 of each live head write its 128 channels (32 per
@@ -532,20 +555,22 @@ struct MfmaSoftmax {
   template <int G>
   __device__ void store(CombineLds<G>& cl, int wave, int lane, float sm_scale) const {
     const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
+    // accumulator column col holds head hc (one tile, copy gc == 0) or head col
+    const int h_o = NT == 1 ? hc : col;
+    if ((NT == 1 ? gc == 0 : true) && h_o < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = &cl.o[wave][h_o][32 * ks + 8 * i];
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0][0][i], o[0][1][i], o[0][2][i], o[0][3][i]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[0][4][i], o[0][5][i], o[0][6][i], o[0][7][i]);
+      }
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int h = 4 * n + hc;
-      if (gc == 0 && h < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float* dst = &cl.o[wave][h][32 * ks + 8 * i];
-          *reinterpret_cast<float4*>(dst) = make_float4(o[n][0][i], o[n][1][i], o[n][2][i], o[n][3][i]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(o[n][4][i], o[n][5][i], o[n][6][i], o[n][7][i]);
-        }
-        if (ks == 0) {
-          cl.m[wave][h] = m[n] * sm_scale;
-          cl.l[wave][h] = l[n];
-        }
+      if (gc == 0 && h < G && ks == 0) {
+        cl.m[wave][h] = m[n] * sm_scale;
+        cl.l[wave][h] = l[n];
       }
     }
   }
