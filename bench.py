@@ -2,9 +2,9 @@
 """Benchmark one FFD decode-attention step on one MI355X; prints one JSON line.
 
 A step is the whole hot path for one layer: pseudo-max, fused Top-delta scan +
-refine, log-sum-exp merge, over inputs already resident in HBM: three kernel
-launches, or two on short caches, where the pseudo-max work-groups lead the
-scan + refine launch (ffd_plan_pseudomax).  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
+refine, log-sum-exp merge, over inputs already resident in HBM: two kernel
+launches, the pseudo-max work-groups leading the scan + refine launch
+(ffd_plan_pseudomax; three launches where the pseudo-max has its own).  Defaults: the Llama-3.1-8B-like 16K decode layer (B=1, Hq=32, Hkv=8,
 delta=5), plus the 256K long-context shape with the in-house dense
 flash-decode kernel timed beside it.
 

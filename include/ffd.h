@@ -136,8 +136,9 @@ typedef struct ffd_cache {
  *                bit 1 is ignored.
  *  pm_mode       where the pseudo-max runs.  0 = the library's choice: inside
  *                the scan + refine launch for the union selection without
- *                run-time termination on short caches (chunk work-groups
- *                <= 1024) when the call enqueues 2 and 4, else its own launch;
+ *                run-time termination when the call enqueues 2 and 4 (and the
+ *                support words fit, see ffd_plan_pseudomax), else its own
+ *                launch;
  *                1 = its own launch; 2 = inside the scan + refine launch;
  *                3 = inside it, but every chunk computes the pseudo-max itself
  *                (the path of a workspace's first call).  2 and 3 need the
@@ -192,7 +193,7 @@ int ffd_cache_bytes(const ffd_shape_t* shape, size_t* codes_bytes, size_t* sz_by
  * work splits).  The workspace holds partial pseudo-maxima and per-chunk
  * attention partials; its contents need no initialisation.  It also carries a
  * step counter from one ffd_decode_attn call to the next: when the pseudo-max
- * runs inside the scan + refine launch (on short caches, see
+ * runs inside the scan + refine launch (the default for a union step, see
  * ffd_debug_t.pm_mode) its results are tagged with that counter.  The first
  * such call on a workspace (or the first after a change of batch, query heads
  * or support size) computes the pseudo-max in every chunk, which is slower;
@@ -215,7 +216,9 @@ int ffd_plan_split(const ffd_shape_t* shape, int32_t* split);
 /* Where the pseudo-max of a whole ffd_decode_attn step (union selection, no
  * debug) runs for `shape` (host call): n_parts = support blocks per sequence
  * (work-groups per KV head), in_grid = 1 when they lead the scan + refine
- * launch, 0 when they have their own launch (see ffd_debug_t.pm_mode). */
+ * launch, 0 when they have their own launch (see ffd_debug_t.pm_mode): in
+ * the grid unless the support parts times query heads per KV head exceed 256
+ * words or the one-dimensional grid would exceed 2^31 - 1 work-groups. */
 int ffd_plan_pseudomax(const ffd_shape_t* shape, int32_t* n_parts, int32_t* in_grid);
 
 /* K-cache pack (Method 1): quantize tokens [t_begin, t_end) of every (b, kv

@@ -20,7 +20,6 @@ static_assert(ffd::kSelectUnion == FFD_SELECT_UNION && ffd::kSelectHeadBlock == 
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr long long kPmgMaxGroups = 1024;  // chunk work-groups up to which the pseudo-max runs in the grid
 // Work-groups per launch the automatic split aims for: about 1.8 rounds of the
 // 768 resident ones (256 CUs x 3), so that fewer, longer work-groups amortise
 // each one's prologue and first memory round trip (at 256K context, 24 blocks
@@ -128,11 +127,14 @@ Plan make_plan(const ffd_shape_t* s, long long target = kTargetGroups, int fixed
 int from_hip(hipError_t e) { return e == hipSuccess ? FFD_OK : FFD_ERR_HIP; }
 
 // default placement of the pseudo-max for a whole union step: inside the
-// attend launch when its words fit one per thread of a work-group and the
-// chunks fit about one round of work-groups on the device (short caches)
+// attend launch whenever its words fit one per thread of a work-group and the
+// grid fits one dimension.  Measured on MI355X the in-grid placement is the
+// faster one at every benchmark shape (16K step 18.6 -> 17.4 us, 256K 65.7 ->
+// 64.7, batched Qwen-like 139.9 -> 136.7, stress 295.2 -> 292.6): a long
+// cache's chunks scan before they need the maxima, so they never wait.
 bool pm_default_in_grid(const ffd_shape_t* s, const Plan& pl) {
   const bool fits = (long long)pl.npart * (s->num_q_heads / s->num_kv_heads) <= 256;
-  return fits && (long long)pl.nchunk * s->num_kv_heads * s->batch <= kPmgMaxGroups;
+  return fits && (long long)(pl.npart + pl.nchunk) * s->num_kv_heads * s->batch < (1ll << 31);
 }
 
 // run-time termination: the call's stream length (0 = the default), or -1
@@ -451,10 +453,7 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
   // Pseudo-max inside the attend launch: possible for the union selection
   // without run-time termination, when the call also enqueues the merge (which
   // advances the epoch of the published words) and the words fit one per
-  // thread of a work-group.  Chosen by default only when the chunks fit about
-  // one round of work-groups on the device (short caches): there the separate
-  // launch's latency is on the critical path, while on long caches the chunks
-  // that start with the pseudo-max work-groups would wait for them.  The
+  // thread of a work-group; the default then (pm_default_in_grid).  The
   // magic the merge writes is keyed to the word layout, so words left by
   // another shape are never trusted.
   const bool whole = p.stages == 0 || (p.stages & 6) == 6;
@@ -467,7 +466,7 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
   p.pm_magic = ffd::kPmMagic ^ ((unsigned long long)shape->batch << 40) ^ ((unsigned long long)shape->num_q_heads << 24) ^
                ((unsigned long long)pl.npart << 4);
   // Split path: the union selection without run-time termination, with the
-  // pseudo-max in its own launch; chosen by default on long caches
+  // pseudo-max in its own launch (debug->pm_mode 1); never the default
   // (split_default), forced on or off by debug->split_mode 2 / 1.
   const bool split_ok = selection == FFD_SELECT_UNION && o.art_patience == 0 && !p.pm_in_grid &&
                         split_possible(shape, pl);
