@@ -257,13 +257,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const __amdgpu_buffer_rsrc_t r_res = make_rsrc(p.res + hb * kResBytes, nbc * kResBytes);
   const __amdgpu_buffer_rsrc_t r_rsc = make_rsrc(p.rsc + hb * kRscBytes, nbc * kRscBytes);
   const __amdgpu_buffer_rsrc_t r_v = make_rsrc(p.v + head * p.L_cap * kHeadDim, nbc * kVBytes);
+  // j < 0: the same instructions through descriptors of size 0, which return
+  // zeros without a memory access (a refine loop's load past the last block:
+  // the load counters stay exact, and nothing is left to wait for)
+  const __amdgpu_buffer_rsrc_t r_none = make_rsrc(p.res, 0);
   auto load_block = [&](int j, RefineRegs& x) {
-    const uint32_t blk = (uint32_t)blk_of(j);
+    const bool live = j >= 0;
+    const uint32_t blk = live ? (uint32_t)blk_of(j) : 0u;
+    const __amdgpu_buffer_rsrc_t rr = live ? r_res : r_none, rs = live ? r_rsc : r_none, rv = live ? r_v : r_none;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64<kNonTemporal>(r_res, (uint32_t)to.res + g * 2048, blk * kResBytes);
-    x.S8 = buf_load_b64<kNonTemporal>(r_rsc, (uint32_t)to.rsc, blk * kRscBytes);
+    for (int g = 0; g < kGroups; ++g) x.R[g] = buf_load_b64<kNonTemporal>(rr, (uint32_t)to.res + g * 2048, blk * kResBytes);
+    x.S8 = buf_load_b64<kNonTemporal>(rs, (uint32_t)to.rsc, blk * kRscBytes);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(r_v, v_lane + 16 * q, blk * kVBytes);
+    for (int q = 0; q < 4; ++q) x.V[q] = buf_load_b128(rv, v_lane + 16 * q, blk * kVBytes);
   };
   // Blocks always kept (sink and local window) are known before any threshold:
   // the refine takes them first (the union selection without run-time
@@ -651,8 +657,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     // kept blocks from the (wave-uniform) masks: the forced ones first, then
     // the others, each in increasing order (under run-time termination all in
     // increasing order).  The next block is loaded while the current one is
-    // computed, unconditionally as in the scan (the last block is re-read
-    // past the end of the list).
+    // computed, unconditionally as in the scan (past the end of the list
+    // through the empty descriptors, so no memory is read and the last
+    // block's wait is not held up).
     uint64_t rem_f = kForcedFirst ? (kmask & fmask) : 0ull, rem_o = kForcedFirst ? (kmask & ~fmask) : kmask;
     auto pop = [&]() -> int {
       if (rem_f) {
@@ -672,13 +679,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       if (!(kForcedFirst && fmask)) load_block(jx, X);  // (else loaded before the scan)
       while (true) {
         const int jy = pop();
-        load_block(jy >= 0 ? jy : jx, Y);
+        load_block(jy, Y);
         refine(jx, X);
         if constexpr (ART)
           if (art_stop()) break;
         if (jy < 0) break;
         const int jn = pop();
-        load_block(jn >= 0 ? jn : jy, X);
+        load_block(jn, X);
         refine(jy, Y);
         if constexpr (ART)
           if (art_stop()) break;
