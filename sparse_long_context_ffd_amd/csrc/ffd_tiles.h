@@ -400,23 +400,31 @@ struct CombineLds {
 
 // Combine the 4 waves' states (stored in `cl`) into the chunk partial
 // (o[128], m, l) of every query head of the group.
+// Every LDS word is read up front and the waves' terms are selected, not
+// branched on, so the reads go out together (a chain of dependent reads under
+// per-wave branches cost about a microsecond per work-group).
 template <int G>
 __device__ void combine_chunk(const DecodeParams& p, const CombineLds<G>& cl, int tid, int b, int hkv, int chunk) {
   const int qh0 = hkv * G;
   for (int i = tid; i < G * kHeadDim; i += 256) {
     const int h = i >> 7, ch = i & 127;
+    float lw[kWaves], mw[kWaves], ow[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lw[w] = cl.l[w][h];
+      mw[w] = cl.m[w][h];
+      ow[w] = cl.o[w][h][ch];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (cl.l[w][h] > 0.f) M = fmaxf(M, cl.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = lw[w] > 0.f ? fmaxf(M, mw[w]) : M;
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      if (cl.l[w][h] > 0.f) {
-        const float f = exp2f((cl.m[w][h] - M) * kLog2e);
-        lsum += cl.l[w][h] * f;
-        o += cl.o[w][h][ch] * f;
-      }
+      const bool live = lw[w] > 0.f;
+      const float f = exp2f(((live ? mw[w] : M) - M) * kLog2e);
+      lsum = live ? fmaf(lw[w], f, lsum) : lsum;
+      o = live ? fmaf(ow[w], f, o) : o;
     }
     const size_t row = ((size_t)b * p.Hq + qh0 + h) * p.nchunk + chunk;
     if (lsum > 0.f) p.part_o[row * kHeadDim + ch] = o;
