@@ -345,6 +345,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const uint32_t pm_want = (uint32_t)pm_epoch + 1u;
   const bool pm_trusted = PMG && pm_magic == p.pm_magic && !p.pm_local;
   bool pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+  const bool pm_had = pm_mine;  // (a second load of a missing word goes out after the scan)
   if (pm_trusted && !pm_mine) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
@@ -425,7 +426,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   if constexpr (PMG) {
     bool pm_fb = false;
     {
+      // a missing word is loaded once more now, while the load issued before
+      // the scan is checked; a stale first copy then waits only for this one
+      unsigned long long pw2 = pw;
+      if (pm_trusted && !pm_had) pw2 = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+      if (!pm_mine) {
+        pw = pw2;
+        pm_mine = (uint32_t)(pw >> 32) == pm_want;
+      }
       int all = __syncthreads_and(pm_trusted && pm_mine);
       for (int s = 0; !all && pm_trusted && s < kPmSpin; ++s) {
         __builtin_amdgcn_s_sleep(8);

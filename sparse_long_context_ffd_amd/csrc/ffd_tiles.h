@@ -160,11 +160,14 @@ struct QFrags {
     const uint32_t z[4] = {zs.x, zs.y, zs.z, zs.w};
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f4 c = cinit_t[nt];
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][0], a0, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][1], a1, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][2], a2, c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][3], a3, c, 0, 0, 0);
+      // MFMA g adds to the rows of group g only (exact zeros elsewhere), so the
+      // four run on their own accumulators, back to back, and row g is taken
+      // from the g-th: the same bits as one accumulator chained through all four
+      const f4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][0], a0, cinit_t[nt], 0, 0, 0);
+      const f4 c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][1], a1, cinit_t[nt], 0, 0, 0);
+      const f4 c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][2], a2, cinit_t[nt], 0, 0, 0);
+      const f4 c3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(B[nt][3], a3, cinit_t[nt], 0, 0, 0);
+      const f4 c = {c0[0], c1[1], c2[2], c3[3]};
       // zero-point terms first (they do not wait for the MFMA), then the
       // scale terms
       float acc = 0.f;
@@ -421,10 +424,12 @@ __device__ void combine_chunk(const DecodeParams& p, const CombineLds<G>& cl, in
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
+      // a wave with l = 0 never weighted a token: its o is +0 and it adds +0,
+      // which leaves the sums unchanged (they are never -0)
       const bool live = lw[w] > 0.f;
-      const float f = exp2f(((live ? mw[w] : M) - M) * kLog2e);
-      lsum = live ? fmaf(lw[w], f, lsum) : lsum;
-      o = live ? fmaf(ow[w], f, o) : o;
+      const float f = live ? exp2f((mw[w] - M) * kLog2e) : 0.f;
+      lsum = fmaf(lw[w], f, lsum);
+      o = fmaf(ow[w], f, o);
     }
     const size_t row = ((size_t)b * p.Hq + qh0 + h) * p.nchunk + chunk;
     if (lsum > 0.f) p.part_o[row * kHeadDim + ch] = o;
