@@ -4,13 +4,17 @@
 //
 // Page: "Faster Than Flash" (gist.science summary of arXiv 2609.00097).
 //   Method 2 (Top-delta): keep when s >= m~ - delta, m~ from sink + local tokens.
-//   Method 3 stage 1, pseudo-max estimation               -> pseudomax_kernel
+//   Method 3 stage 1, pseudo-max estimation               -> pm_group (leading
+//                                                             work-groups of the
+//                                                             attend grid), or
+//                                                             pseudomax_kernel
 //   Method 3 stage 2, stream the 2-bit keys, provisional
 //            scores, filter blocks against the threshold   -> attend_kernel phase A
 //   Method 3 stage 3, residuals + values of the selected
 //            blocks, exact attention (reusing the stage-2
 //            scores kept on chip)                          -> attend_kernel phase B
-//   log-sum-exp merge of the per-chunk partials            -> merge_kernel
+//   log-sum-exp merge of the per-chunk partials            -> merge64_kernel,
+//                                                             merge_kernel
 // Template parameters of attend_kernel: SEL chooses what each query head
 // attends inside the kept blocks (the GQA union, its own kept blocks, or its
 // own tokens by the per-token criterion of Method 2), ART the run-time
