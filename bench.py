@@ -225,7 +225,8 @@ def measure_ffd(w, delta, steps, warmup, c, d, torch, sm_scale, flush, with_vari
     base = ffd.PackedCache(shape)
     ffd.quantize_k(shape, d["k"], 0, w.max_len, base)
     ffd.pack_v(shape, d["v"], 0, w.max_len, base)
-    ws = torch.empty(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(ffd.workspace_bytes(shape), ffd.workspace_bytes_ex(shape, art=ART)), dtype=torch.uint8,
+                     device="cuda")
     out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
     nb = w.max_len // 64
     keep = torch.zeros((w.batch, w.kv_heads, nb), dtype=torch.uint8, device="cuda")
@@ -493,6 +494,76 @@ def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True,
     return out
 
 
+# run-time termination operating points (tau, phi, patience, stream blocks):
+# from the bench's variant (loose) to settings that stop only once the running
+# output has nearly stopped moving; 4-block streams give the 16K step as many
+# work-groups as the union split (the default 16-block streams run 4x fewer)
+ART_POINTS = ((0.05, 0.01, 1, 4), (0.02, 0.005, 2, 4), (0.01, 0.002, 2, 4), (0.005, 0.001, 3, 4),
+              (0.005, 0.001, 3, 16))
+
+
+def art_tradeoff(w, delta, steps, warmup, seed, torch, sm_scale, flush):
+    """Run-time termination on workload `w`: per operating point the step time,
+    the fraction of kept (query head, token) pairs actually folded in, and the
+    output's error against full attention over K-hat (delta = +inf) beside the
+    union step's own error at the same delta, so that a point can be chosen
+    for an accuracy budget.  Same rotation and flush as every other leg."""
+    import sparse_long_context_ffd_amd as ffd
+    c, d = prepare(w, seed, torch)
+    shape = ffd.make_shape(w.batch, w.q_heads, w.kv_heads, w.max_len, sink=w.sink, local=w.local)
+    base = ffd.PackedCache(shape)
+    ffd.quantize_k(shape, d["k"], 0, w.max_len, base)
+    ffd.pack_v(shape, d["v"], 0, w.max_len, base)
+    ws = torch.empty(max([ffd.workspace_bytes(shape)] + [ffd.workspace_bytes_ex(shape, art=a) for a in ART_POINTS]),
+                     dtype=torch.uint8, device="cuda")
+    rows = (w.batch, w.q_heads, 128)
+    full, ref = (torch.empty(rows, dtype=torch.float16, device="cuda") for _ in range(2))
+    ffd.decode_attn(shape, d["q"], base, d["seq_lens"], math.inf, sm_scale, full, ws)
+    ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, ref, ws)
+    lens = d["seq_lens"].long()
+    valid = torch.arange(w.max_len, device="cuda")[None, :] < lens[:, None]
+    tok_total = int(lens.sum()) * w.kv_heads
+    # kept (query head, token) pairs of the union step; termination only ever
+    # folds in a subset of them.  The rotation is sized from the union step's
+    # bytes, as for the other legs.
+    tu = torch.zeros((w.batch, w.q_heads, w.max_len), dtype=torch.uint8, device="cuda")
+    ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, ref, ws, debug={"tmask": tu})
+    torch.cuda.synchronize()
+    kept_pairs = ((tu == 1) & valid[:, None, :]).sum().item()
+    del tu
+    layer_bytes = sum(ffd.cache_bytes(shape).values())
+    R = copies_for(SCAN_BYTES * tok_total + REFINE_BYTES * kept_pairs // w.group, layer_bytes)
+    layers = [base] + [base.clone() for _ in range(R - 1)]
+
+    def err(o):
+        dd = o.float() - full.float()
+        return round((dd.norm() / full.float().norm()).item(), 6)
+
+    out = {"workload": w.name, "delta": delta, "union_rel_l2_vs_full": err(ref), "layers_rotated": R, "points": []}
+    g = graph_of([lambda i=i: ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, ref,
+                                              ws) for i in range(steps)], torch)
+    g.replay()
+    out["union_us_per_step"] = round(timed_replay(g, torch, flush) * 1e3 / steps, 3)
+    del g
+    for art in ART_POINTS:
+        o = torch.empty(rows, dtype=torch.float16, device="cuda")
+        tm = torch.zeros((w.batch, w.q_heads, w.max_len), dtype=torch.uint8, device="cuda")
+        ffd.decode_attn(shape, d["q"], base, d["seq_lens"], delta, sm_scale, o, ws, debug={"tmask": tm}, art=art)
+        torch.cuda.synchronize()
+        folded = ((tm == 1) & valid[:, None, :]).sum().item()
+        g = graph_of([lambda i=i: ffd.decode_attn(shape, d["q"], layers[i % R], d["seq_lens"], delta, sm_scale, o,
+                                                  ws, art=art) for i in range(steps)], torch)
+        g.replay()
+        us = timed_replay(g, torch, flush) * 1e3 / steps
+        del g
+        out["points"].append({"tau_phi_patience_stream_blocks": list(art), "us_per_step": round(us, 3),
+                              "folded_frac_of_kept": round(folded / max(kept_pairs, 1), 5),
+                              "rel_l2_vs_full": err(o)})
+    del layers, base, c, d
+    torch.cuda.empty_cache()
+    return out
+
+
 def sweep_workload(L):
     """The Llama-8B-like decode layer (B=1, Hq=32, Hkv=8, delta 5) at context L,
     with the needle count of the 16K and 256K workloads' rule 16 * sqrt(L / 16K)."""
@@ -546,7 +617,7 @@ def cpu_baseline(w, delta, c, sm_scale, budget_s=10.0):
             "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
-LEGS = ("long", "qwen", "stress", "sweep")
+LEGS = ("long", "qwen", "stress", "sweep", "art")
 
 
 def main():
@@ -677,6 +748,11 @@ def main():
             "points": pts,
             "slope_us_per_1k_tokens": {"ffd": round(slope(xs, [p["us_per_step"] for p in pts]), 4),
                                        "dense": round(slope(xs, [p["dense_us_per_step"] for p in pts]), 4)}}
+
+    if "art" in legs:
+        result["art_tradeoff"] = [art_tradeoff(wa, wa.deltas[0], steps_leg, warm_leg, args.seed, torch, sm_scale,
+                                               flush)
+                                  for wa in (w, WORKLOADS["qwen7b_b16_16k32k"], WORKLOADS["stress_b4_128k"])]
 
     result["hbm_achievable"] = hbm_probe(torch)
     # the attend kernels' rates against the measured streaming-read rate too
