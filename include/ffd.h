@@ -203,7 +203,7 @@ int ffd_workspace_bytes(const ffd_shape_t* shape, size_t* bytes);
 
 /* Work split ffd_decode_attn chooses for `shape`: blocks per work-group and
  * chunks per sequence (host call).  shape->chunk_blocks > 0 forces the blocks
- * per work-group (capped at 32, or 16 when a KV head serves more than 4 query
+ * per work-group (capped at 32, or 24 when a KV head serves more than 4 query
  * heads); otherwise about 1380 work-groups per launch, at most 4 blocks each
  * on short caches.  ffd_dense_decode_attn aims at about 2048 instead. */
 int ffd_plan(const ffd_shape_t* shape, int32_t* chunk_blocks, int32_t* n_chunks);

@@ -74,7 +74,7 @@ struct Plan {
 Plan make_plan(const ffd_shape_t* s, long long target = kTargetGroups, int fixed_cb = 0) {
   Plan p;
   const int G = s->num_q_heads / s->num_kv_heads;
-  const int cb_max = G <= 4 ? 32 : 16;
+  const int cb_max = G <= 4 ? 32 : 24;
   p.nblk_cap = s->max_seq_len / 64;
   long long cb;
   if (fixed_cb > 0) {

@@ -120,7 +120,7 @@ __device__ void pm_group(const DecodeParams& p, int part, int hkv, int b, uint32
 template <int G>
 struct AttendCfg {
   static constexpr int NT = QFrags<G>::NT;
-  static constexpr int CBMAX = (G <= 4) ? 32 : 16;
+  static constexpr int CBMAX = (G <= 4) ? 32 : 24;
   static constexpr size_t est_bytes(int cb) { return (size_t)cb * kWaves * G * 16 * sizeof(float); }
   static constexpr size_t tmax_bytes(int cb) { return (size_t)cb * 4 * kWaves * G * sizeof(float); }
   // the block-max diagnostic's area is allocated only when it is requested

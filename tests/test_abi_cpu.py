@@ -301,15 +301,15 @@ def test_plan_pseudomax(B, Hq, Hkv, L):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,expect", [(1, 32, 8, 16384, 4), (1, 32, 8, 262144, 24),
-                                               (16, 28, 4, 32768, 16), (1, 4, 1, 4096, 1),
+                                               (16, 28, 4, 32768, 24), (1, 4, 1, 4096, 1),
                                                (4, 32, 8, 131072, 32), (1, 1, 1, 64, 1)])
 def test_automatic_split(B, Hq, Hkv, L, expect):
     """About 1380 work-groups per launch on long caches, up to 4 blocks per work-group on
-    short ones; at most 32 blocks per chunk (16 when G > 4)."""
+    short ones; at most 32 blocks per chunk (24 when G > 4)."""
     cb, nch = ffd.plan(ffd.make_shape(B, Hq, Hkv, L))
     assert cb == expect and nch == math.ceil(L // 64 / cb)
     cb, nch = ffd.plan(ffd.make_shape(B, Hq, Hkv, L, chunk_blocks=10 ** 6))
-    cap = 32 if Hq // Hkv <= 4 else 16
+    cap = 32 if Hq // Hkv <= 4 else 24
     assert cb == min(cap, L // 64) and nch == math.ceil(L // 64 / cb)
 
 

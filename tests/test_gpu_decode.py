@@ -79,6 +79,15 @@ def test_decode_group_sizes_and_ragged_lengths(G, L):
     _run(w, 0, [3.0, 0.5], fill=0xFF)
 
 
+@pytest.mark.parametrize("G,cb", [(5, 24), (8, 24), (7, 13)])
+def test_decode_large_groups_at_the_chunk_cap(G, cb):
+    """G > 4 at the largest chunk (24 blocks: 48-62 KB of estimates in LDS per
+    work-group) and at a size with a partial last batch; 47 blocks in two or
+    four chunks, so the chunks hold 23-24 and 11-12 blocks."""
+    w = Workload(f"g{G}_cb{cb}", 2, 2 * G, 2, 3072, 3000, deltas=(3.0,), needles=4)
+    _run(w, 0, [3.0], chunk_blocks=cb, fill=0xFF)
+
+
 def test_decode_sink_and_local_variants():
     w = WORKLOADS["tiny_h4x1_4k"]
     _run(w, 2, [2.0], sink=0, local=64)
