@@ -229,6 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
   // h) under the per-head block selection
   __shared__ int kflag[kWaves][CBMAX];
+  __shared__ __align__(16) int vote[2][kWaves];  // per-wave votes of wg_all (two sets, used in turn)
   __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
@@ -439,20 +440,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         pw = pw2;
         pm_mine = (uint32_t)(pw >> 32) == pm_want;
       }
-      int all = __syncthreads_and(pm_trusted && pm_mine);
+      // The thread's part goes to LDS before the vote, so that one barrier
+      // publishes both; a value whose word is stale is never read (the
+      // work-group then takes the fallback below, which rewrites what it reads).
+      pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
+      bool all = wg_all(pm_trusted && pm_mine, vote[0], wave, lane);
       for (int s = 0; !all && pm_trusted && s < kPmSpin; ++s) {
         __builtin_amdgcn_s_sleep(8);
         if (!pm_mine) {
           pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           pm_mine = (uint32_t)(pw >> 32) == pm_want;
         }
-        all = __syncthreads_and(pm_mine);
+        pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
+        all = wg_all(pm_mine, vote[(s + 1) & 1], wave, lane);
       }
       pm_fb = !all;
-      pm_t = (tid < n_pm && !pm_fb) ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
     }
-    pm_s[tid] = pm_t;
-    __syncthreads();
     if (pm_fb) {
       float m = -INFINITY;  // (threads tid < G) head tid
       for (int part = 0; part < p.npart; ++part) {

@@ -140,6 +140,18 @@ __device__ inline uint32_t opaque_vgpr(uint32_t k) {
 }
 __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { return (x & mask) | bits; }
 
+// True in every thread iff `pred` holds in every thread of a work-group of
+// four waves: one vote per wave in `vote` (4 ints in LDS, 16-byte aligned) and
+// one barrier.  Consecutive calls must alternate between two vote arrays (a
+// wave past the barrier may write its next vote while another still reads).
+__device__ inline bool wg_all(bool pred, int* vote, int wave, int lane) {
+  const bool w = __builtin_amdgcn_ballot_w64(!pred) == 0;
+  if (lane == 0) vote[wave] = w ? 1 : 0;
+  __syncthreads();
+  const int4 v = *reinterpret_cast<const int4*>(vote);
+  return (v.x & v.y & v.z & v.w) != 0;
+}
+
 // maximum over all 64 lanes, returned in every lane
 __device__ inline float wave_max(float v) {
   v = fmaxf(v, dpp<kQuadXor1>(v));

@@ -409,15 +409,28 @@ struct CombineLds {
 template <int G>
 __device__ void combine_chunk(const DecodeParams& p, const CombineLds<G>& cl, int tid, int b, int hkv, int chunk) {
   const int qh0 = hkv * G;
-  for (int i = tid; i < G * kHeadDim; i += 256) {
+  // all LDS reads first (they go out together), then the arithmetic
+  constexpr int kIt = (G * kHeadDim + 255) / 256;
+  float lwk[kIt][kWaves], mwk[kIt][kWaves], owk[kIt][kWaves];
+#pragma unroll
+  for (int k = 0; k < kIt; ++k) {
+    const int i = min(tid + 256 * k, G * kHeadDim - 1);
     const int h = i >> 7, ch = i & 127;
-    float lw[kWaves], mw[kWaves], ow[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      lw[w] = cl.l[w][h];
-      mw[w] = cl.m[w][h];
-      ow[w] = cl.o[w][h][ch];
+      lwk[k][w] = cl.l[w][h];
+      mwk[k][w] = cl.m[w][h];
+      owk[k][w] = cl.o[w][h][ch];
     }
+  }
+#pragma unroll
+  for (int k = 0; k < kIt; ++k) {
+    const int i = tid + 256 * k;
+    if (i >= G * kHeadDim) break;
+    const int h = i >> 7, ch = i & 127;
+    const float(&lw)[kWaves] = lwk[k];
+    const float(&mw)[kWaves] = mwk[k];
+    const float(&ow)[kWaves] = owk[k];
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = lw[w] > 0.f ? fmaxf(M, mw[w]) : M;
