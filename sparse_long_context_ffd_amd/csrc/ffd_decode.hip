@@ -228,7 +228,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   QFrags<G>::stage_store(qst, tid, qs);
   // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
   // h) under the per-head block selection
-  __shared__ int kflag[kWaves][CBMAX];
+  __shared__ int kflag[kWaves][CBMAX];  // per-head reach bits (per-head block selection)
+  __shared__ uint64_t wkf[kWaves];      // each wave's reach mask (bit j: block j), other selections
+  uint64_t wk = 0;                      // this wave's reach mask (wave-uniform)
   __shared__ __align__(16) int vote[2][kWaves];  // per-wave votes of wg_all (two sets, used in turn)
   __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
@@ -250,8 +252,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // Drain every load issued so far (first batch, q, the pseudo-max parts) so
   // that the pipelined scan below starts from an exact count of loads in flight.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  if constexpr (!PMG) pm_s[tid] = pm_t;
-  __syncthreads();  // q staged in LDS (and the partial maxima without PMG)
+  // In-grid pseudo-max: every word must carry this step's tag (epoch + 1).
+  // When every word was already there in the prologue (work-groups that start
+  // after the pseudo-max work-groups have published), the thresholds are
+  // known before the scan and the blocks are decided as they are scanned.
+  // Otherwise (usually at the start of the grid) the words still missing are
+  // loaded again before the scan and checked after it, where the thresholds
+  // are first needed; words still missing then are polled a bounded number
+  // of times, after which (or before the merge has initialised the sync
+  // words, or under pm_local) the work-group computes the pseudo-max itself.
+  // All conditions are work-group uniform.
+  const uint32_t pm_want = (uint32_t)pm_epoch + 1u;
+  const bool pm_trusted = PMG && pm_magic == p.pm_magic && !p.pm_local;
+  bool pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+  bool pm_early = false;
+  if constexpr (PMG) {
+    // the thread's part goes to LDS with its vote; the vote's barrier also
+    // publishes q (a part whose word is stale is never read)
+    pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
+    pm_early = wg_all(pm_trusted && pm_mine, vote[0], wave, lane);
+  } else {
+    pm_s[tid] = pm_t;
+    __syncthreads();  // q staged in LDS, and the partial maxima
+  }
   // Refine loads of a block: residual, its scales, V.
   // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes).
   // The residual and its scales load with the non-temporal hint (a wave's
@@ -338,18 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     }
     if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
   };
-  if constexpr (!PMG) compute_thresholds();
-  // In-grid pseudo-max: every word must carry this step's tag (epoch + 1).
-  // The words loaded in the prologue are usually not there yet (their
-  // work-groups started with this one), so the words still missing are loaded
-  // again before the scan and checked after it, where the thresholds are
-  // first needed; words still missing then are polled a bounded number of
-  // times, after which (or before the merge has initialised the sync words, or
-  // under pm_local) the work-group computes the pseudo-max itself.  All
-  // conditions are work-group uniform.
-  const uint32_t pm_want = (uint32_t)pm_epoch + 1u;
-  const bool pm_trusted = PMG && pm_magic == p.pm_magic && !p.pm_local;
-  bool pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
+  if (!PMG || pm_early) compute_thresholds();
   const bool pm_had = pm_mine;  // (a second load of a missing word goes out after the scan)
   if (pm_trusted && !pm_mine) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
@@ -374,12 +386,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
         }
         // per-head block selection: bit h = head h reaches its threshold in
         // this tile (lanes 16*ks .. 16*ks + 15 hold head 4*nt + ks); otherwise
-        // one flag for the group (without PMG; with it after the scan)
+        // bit j of the wave's reach mask: some head of the group reaches it
+        // (without PMG; with it after the scan)
         uint32_t hreach = 0;
         bool reach = false;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if constexpr (!PMG) {
+          if (!PMG || pm_early) {
             if constexpr (SEL == kSelectHeadBlock) {
               const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
               hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
@@ -398,9 +411,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
             if (h < G && (col & 3) == 0) tmax[(j * 4 * kWaves + 4 * wave + (col >> 2)) * G + h] = qm;
           }
         }
-        if constexpr (!PMG) {
-          if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
-          if (lane == 0) kflag[wave][j] = (int)hreach;
+        if (!PMG || pm_early) {
+          if constexpr (SEL == kSelectHeadBlock) {
+            if (lane == 0) kflag[wave][j] = (int)hreach;
+          } else {
+            wk |= __builtin_amdgcn_ballot_w64(reach) != 0 ? 1ull << j : 0ull;
+          }
         }
       }
     }
@@ -428,7 +444,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   }
 
   // ---- PMG: pseudo-maxima, thresholds and the reach flags after the scan ----
-  if constexpr (PMG) {
+  if (PMG && !pm_early) {
     bool pm_fb = false;
     {
       // a missing word is loaded once more now, while the load issued before
@@ -444,7 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
       // publishes both; a value whose word is stale is never read (the
       // work-group then takes the fallback below, which rewrites what it reads).
       pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
-      bool all = wg_all(pm_trusted && pm_mine, vote[0], wave, lane);
+      bool all = wg_all(pm_trusted && pm_mine, vote[1], wave, lane);
       for (int s = 0; !all && pm_trusted && s < kPmSpin; ++s) {
         __builtin_amdgcn_s_sleep(8);
         if (!pm_mine) {
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
           pm_mine = (uint32_t)(pw >> 32) == pm_want;
         }
         pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
-        all = wg_all(pm_mine, vote[(s + 1) & 1], wave, lane);
+        all = wg_all(pm_mine, vote[s & 1], wave, lane);
       }
       pm_fb = !all;
     }
@@ -473,7 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     compute_thresholds();
 
     // ---- reach flags from the stored estimates, now that the thresholds are
-    // known: per head, or one flag for the group (lanes 16*ks .. 16*ks + 15
+    // known: per head, or one bit per block for the group (lanes 16*ks .. 16*ks + 15
     // hold head 4*nt + ks; each lane reads back the estimates it stored).  The
     // reads go out 8 blocks at a time (indices clamped to the chunk).
     for (int j0 = 0; j0 < nbl; j0 += 8) {
@@ -503,12 +519,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
               reach = reach || (e8[v][nt] >= thr_t[nt]);
             }
           }
-          if constexpr (SEL != kSelectHeadBlock) hreach = __builtin_amdgcn_ballot_w64(reach) != 0 ? 1u : 0u;
-          if (lane == 0) kflag[wave][j0 + v] = (int)hreach;
+          if constexpr (SEL == kSelectHeadBlock) {
+            if (lane == 0) kflag[wave][j0 + v] = (int)hreach;
+          } else {
+            wk |= __builtin_amdgcn_ballot_w64(reach) != 0 ? 1ull << (j0 + v) : 0ull;
+          }
         }
       }
     }
   }
+  if constexpr (SEL != kSelectHeadBlock)
+    if (lane == 0) wkf[wave] = wk;
   __syncthreads();
 
   // ---- block decisions (every wave derives the same mask) ----
@@ -518,9 +539,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     bool kp = false;
     if (lane < nbl) {
       const int blk = blk_of(lane);
-      // the four flags are read unconditionally (one LDS round trip, not a
-      // chain of short-circuit reads)
-      const int any = kflag[0][lane] | kflag[1][lane] | kflag[2][lane] | kflag[3][lane];
+      // the four waves' flags are read unconditionally (one LDS round trip,
+      // not a chain of short-circuit reads)
+      int any;
+      if constexpr (SEL == kSelectHeadBlock)
+        any = kflag[0][lane] | kflag[1][lane] | kflag[2][lane] | kflag[3][lane];
+      else
+        any = (int)(((wkf[0] | wkf[1]) | (wkf[2] | wkf[3])) >> lane) & 1;
       kp = blk < sink_end || blk >= local_beg || any != 0;
       if (wave == 0) {
         if (p.dbg_keep) p.dbg_keep[head * p.nblk_cap + blk] = kp ? 1 : 0;
