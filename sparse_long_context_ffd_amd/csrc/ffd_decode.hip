@@ -563,6 +563,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     }
     kmask = __builtin_amdgcn_ballot_w64(kp);
   }
+  if (PMG && kmask == 0) {
+    // Nothing kept (so no forced block and no refine load in flight): the
+    // chunk's partial is empty; write it as the combine would (weight 0 in
+    // the merge, o never read) and free the slot.  In-grid launches only (in
+    // the others the early exit costs the run-time termination kernels spills).
+    if (tid < G) p.part_ml[((size_t)b * p.Hq + qh0 + tid) * p.nchunk + chunk] = make_float2(-INFINITY, 0.f);
+    return;
+  }
 
   // ---- phase B: refine tile `wave` of every kept block ----
   MfmaSoftmax<NT> st;
