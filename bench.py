@@ -76,13 +76,13 @@ FLUSH_BYTES = 1 << 30         # the pre-replay copy: 1 GiB read + 1 GiB written
 # `bench.py --workload W --no-long --no-variants --no-cpu-baseline --steps 20 --warmup 5`
 # (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the dispatches of
 # the attend kernel the step runs).  Both counters are scaled by what they read for the plain
-# 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088.5 KiB
+# 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088.6 KiB
 # for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
 # while the kernel sources hash to the digest it was recorded with.
-FETCH_SCALE, WRITE_SCALE = 262144 / 131088.5, 1.0
+FETCH_SCALE, WRITE_SCALE = 262144 / 131088.6, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "ca79af7196dc127b", "fetch": 10250.75, "write": 695.5},
-    "long_256k": {"sources": "ca79af7196dc127b", "fetch": 133855.75, "write": 2463.56},
+    "llama8b_16k": {"sources": "af71b0047c026b29", "fetch": 10258.69, "write": 695.62},
+    "long_256k": {"sources": "af71b0047c026b29", "fetch": 133902.5, "write": 2464.59},
 }
 REPLAYS = 10  # replays of the K-step graph behind the reported spread (the first is the timed one)
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
