@@ -115,16 +115,16 @@ def test_art_streams_follow_the_call_not_the_batch_or_capacity():
     """The same sequences and queries visit the same blocks and give the same
     output bits alone (batch 1), inside a batch of 16, and at three cache
     capacities: the streams come from the call's stream length, not from the
-    occupancy split of the launch.  The largest capacity has more than 64
-    streams per sequence, so its log-sum-exp merge runs in the general merge
-    kernel, the others in the 64-partial one: both must give the same bits."""
+    occupancy split of the launch.  The capacities have 12 to 256 streams per
+    sequence, so the log-sum-exp merge runs in the one-wave kernel for up to
+    64 partials and in the general one: both must give the same bits."""
     import sparse_long_context_ffd_amd as ffd
     torch = torch_mod()
     G, Hkv, L, delta, art = 4, 2, 3000, 3.0, (0.05, 0.01, 1, 4)
     w1 = Workload("art_same_b1", 1, G * Hkv, Hkv, 3008, L, needles=4)
     c1 = make_case(w1, 7)
     runs = []
-    for B, L_cap, b0 in [(1, 3008, 0), (1, 8192, 0), (16, 4096, 9), (16, 8192, 2), (1, 32768, 0)]:
+    for B, L_cap, b0 in [(1, 3008, 0), (1, 8192, 0), (16, 4096, 9), (16, 8192, 2), (1, 32768, 0), (1, 65536, 0)]:
         rng = np.random.default_rng([B, L_cap])
         q = rng.standard_normal((B, G * Hkv, 128)).astype(np.float16)
         k = rng.standard_normal((B, Hkv, L_cap, 128)).astype(np.float16)
@@ -154,4 +154,33 @@ def test_art_streams_follow_the_call_not_the_batch_or_capacity():
             assert np.array_equal(vis0[h], r["visited"]), f"h{h}: visited blocks differ from the oracle's"
         d = out0[h * G:(h + 1) * G] - orc.decode_head(c1["q"][0, h * G:(h + 1) * G], pk, c1["v"][0, h], L, delta,
                                                       SM_SCALE, keep=vis0[h])["out"]
+        assert np.abs(d).max() <= ATOL
+
+
+def test_merge_of_more_than_64_live_partials():
+    """A sequence with 79 live termination streams (more partials than the
+    one-wave merge takes, so the general merge kernel runs) gives the same
+    bits at capacities of 79 and 256 streams, and the oracle's output under
+    the visited blocks."""
+    import sparse_long_context_ffd_amd as ffd
+    torch = torch_mod()
+    G, Hkv, L, delta, art = 4, 2, 20000, 2.0, (0.05, 0.01, 1, 4)
+    w1 = Workload("art_many_partials", 1, G * Hkv, Hkv, 20032, L, needles=8)
+    c1 = make_case(w1, 11)
+    outs = []
+    for L_cap in (20032, 65536):
+        k = np.zeros((1, Hkv, L_cap, 128), np.float16)
+        v = np.zeros_like(k)
+        k[:, :, :20032], v[:, :, :20032] = c1["k"], c1["v"]
+        shape = ffd.make_shape(1, G * Hkv, Hkv, L_cap)
+        cache = gpu_pack(shape, dev(k, torch), dev(v, torch))
+        say(f"art many partials: L_cap={L_cap} (plan {ffd.plan(shape)})")
+        got = gpu_decode(shape, dev(c1["q"], torch), cache, dev(c1["seq_lens"], torch), delta, torch, art=art)
+        outs.append(got)
+    assert np.array_equal(outs[0]["out"], outs[1]["out"]), "the output bits depend on the capacity"
+    for h in range(Hkv):
+        vis = _visited(outs[0], 0, h, G, L, f"h{h}")
+        pk = orc.quantize_k(c1["k"][0, h])
+        d = outs[0]["out"][0, h * G:(h + 1) * G] - orc.decode_head(c1["q"][0, h * G:(h + 1) * G], pk, c1["v"][0, h],
+                                                                   L, delta, SM_SCALE, keep=vis)["out"]
         assert np.abs(d).max() <= ATOL
