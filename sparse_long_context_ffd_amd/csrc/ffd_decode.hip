@@ -226,11 +226,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   }
 
   QFrags<G>::stage_store(qst, tid, qs);
-  // wave's tile of block j reached a threshold: 0/1, or the heads that did (bit
-  // h) under the per-head block selection
-  __shared__ int kflag[kWaves][CBMAX];  // per-head reach bits (per-head block selection)
-  __shared__ uint64_t wkf[kWaves];      // each wave's reach mask (bit j: block j), other selections
-  uint64_t wk = 0;                      // this wave's reach mask (wave-uniform)
+  // Blocks the wave's tile reached a threshold in: under the per-head block
+  // selection the heads that did (bit h of kflag[wave][j]); otherwise bit j of
+  // the wave's reach mask wk, published in wkf[wave] for the decision.
+  __shared__ int kflag[kWaves][CBMAX];
+  __shared__ uint64_t wkf[kWaves];
+  uint64_t wk = 0;  // (wave-uniform)
   __shared__ __align__(16) int vote[2][kWaves];  // per-wave votes of wg_all (two sets, used in turn)
   __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
@@ -566,8 +567,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   if (PMG && kmask == 0) {
     // Nothing kept (so no forced block and no refine load in flight): the
     // chunk's partial is empty; write it as the combine would (weight 0 in
-    // the merge, o never read) and free the slot.  In-grid launches only (in
-    // the others the early exit costs the run-time termination kernels spills).
+    // the merge, o never read) and free the slot.  Only in the in-grid launch:
+    // in the other variants this exit made the run-time termination kernels
+    // spill registers.
     if (tid < G) p.part_ml[((size_t)b * p.Hq + qh0 + tid) * p.nchunk + chunk] = make_float2(-INFINITY, 0.f);
     return;
   }
