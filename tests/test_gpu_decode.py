@@ -356,3 +356,14 @@ def test_dense_workspace_reuse_and_ragged_rows():
                 d = got[b, h * G:(h + 1) * G] - ref
                 assert np.abs(d).max() <= 2e-3 and np.linalg.norm(d) <= 1e-3 * np.linalg.norm(ref), \
                     f"call {r} b{b} h{h}"
+
+
+@pytest.mark.parametrize("q_scale,delta", [(8.0, 5.0), (8.0, math.inf), (0.01, 5.0), (0.01, -1e30)])
+def test_decode_extreme_score_ranges(q_scale, delta):
+    """Queries scaled so that the logits span hundreds of units (one key takes
+    nearly all the weight; the refine's running maximum jumps by far more than
+    its rescale slack) or almost nothing (near-uniform weights over every
+    attended token): mask and output still match the oracle."""
+    w = Workload(f"qscale{q_scale}", 2, 8, 2, 4096, None, len_range=(1500, 4096), deltas=(delta,), needles=6,
+                 q_scale=q_scale)
+    _run(w, 3, [delta])
