@@ -367,3 +367,43 @@ def test_decode_extreme_score_ranges(q_scale, delta):
     w = Workload(f"qscale{q_scale}", 2, 8, 2, 4096, None, len_range=(1500, 4096), deltas=(delta,), needles=6,
                  q_scale=q_scale)
     _run(w, 3, [delta])
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two decode steps with their own workspaces enqueued on two streams
+    without a synchronisation between them give the same bits as the same
+    calls made one after the other: a call keeps all its state in its own
+    workspace and outputs."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    wa = Workload("streams_a", 2, 16, 4, 8192, None, len_range=(3000, 8192), deltas=(5.0,), needles=6)
+    wb = Workload("streams_b", 1, 28, 4, 16384, 16384, deltas=(7.0,), needles=8)
+    runs = []
+    for w, seed in ((wa, 1), (wb, 2)):
+        c = make_case(w, seed)
+        shape = shape_for(w)
+        cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
+        ws = torch.zeros(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+        runs.append((w, shape, dev(c["q"], torch), cache, dev(c["seq_lens"], torch), ws, out))
+    # sequential reference (two calls each, so the second uses published words)
+    ref = []
+    for w, shape, q, cache, lens, ws, out in runs:
+        for _ in range(2):
+            ffd.decode_attn(shape, q, cache, lens, w.deltas[0], SM_SCALE, out, ws)
+        torch.cuda.synchronize()
+        ref.append(out.clone())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for (w, shape, q, cache, lens, ws, out), s in zip(runs, streams):
+            out.zero_()
+        torch.cuda.synchronize()
+        for (w, shape, q, cache, lens, ws, out), s in zip(runs, streams):
+            with torch.cuda.stream(s):
+                ffd.decode_attn(shape, q, cache, lens, w.deltas[0], SM_SCALE, out, ws)
+                ffd.decode_attn(shape, q, cache, lens, w.deltas[0], SM_SCALE, out, ws)
+        torch.cuda.synchronize()
+        for (w, shape, q, cache, lens, ws, out), r in zip(runs, ref):
+            say(f"two streams rep {rep}: {w.name}")
+            assert torch.equal(out, r), f"{w.name}: concurrent result differs from the sequential one"
