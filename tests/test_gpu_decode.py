@@ -407,3 +407,44 @@ def test_concurrent_calls_on_two_streams():
         for (w, shape, q, cache, lens, ws, out), r in zip(runs, ref):
             say(f"two streams rep {rep}: {w.name}")
             assert torch.equal(out, r), f"{w.name}: concurrent result differs from the sequential one"
+
+
+def test_graph_replay_matches_eager_on_a_long_grid():
+    """A decode step of a grid several times larger than the resident
+    work-groups (where later chunks find the pseudo-max already published and
+    decide while they scan) captured in a HIP graph: every replay, with eager
+    work and synchronisations between them, gives the eager call's bits."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    w = Workload("graph_long", 4, 32, 8, 16384, None, len_range=(9000, 16384), deltas=(5.0,), needles=12)
+    c = make_case(w, 6)
+    shape = shape_for(w)
+    cb, nch = ffd.plan(shape)
+    assert nch * w.batch * w.kv_heads > 1024
+    q, lens = dev(c["q"], torch), dev(c["seq_lens"], torch)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
+    ws = torch.zeros(ffd.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out_e = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float16, device="cuda")
+    for _ in range(2):
+        ffd.decode_attn(shape, q, cache, lens, 5.0, SM_SCALE, out_e, ws)
+    torch.cuda.synchronize()
+    ref = out_e.clone()
+    out_g = torch.zeros_like(out_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ffd.decode_attn(shape, q, cache, lens, 5.0, SM_SCALE, out_g, ws)
+    for r in range(4):
+        out_g.zero_()
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"long-grid graph replay {r}")
+        assert torch.equal(out_g, ref), f"replay {r} differs from the eager result"
+        assert torch.isfinite(junk)
+    # and the result is the oracle's on a sampled head
+    got = gpu_decode(shape, q, cache, lens, 5.0, torch)
+    assert np.array_equal(got["out"], ref.float().cpu().numpy())
+    pk = orc.quantize_k(c["k"][2, 5])
+    check_head(orc, c["q"][2, 5 * w.group:6 * w.group], pk, c["v"][2, 5], int(c["seq_lens"][2]), 5.0, got, 2, 5,
+               w.group, label="graph long b2 h5")
