@@ -69,7 +69,7 @@ enum ffd_status {
  * 2^24 (the kernels address one head's 256 bytes of values per token with
  * 32-bit offsets),
  * chunk_blocks >= 0 (0 = library choice; otherwise the number of 64-token
- * blocks one work-group scans and refines, capped at 32 for G <= 4 and 16
+ * blocks one work-group scans and refines, capped at 32 for G <= 4 and 24
  * above; it changes only the summation order of the result, and run-time
  * termination ignores it), batch and
  * num_kv_heads at most 65535 (launch-grid dimensions). */
