@@ -475,6 +475,8 @@ def leg(name, w, delta, steps, warmup, seed, torch, sm_scale, flush, dense=True,
            "us_per_step": round(r["us_per_step"], 3), "us_per_step_spread": r["replay_spread"],
            "keep_fraction": round(r["keep_fraction"], 5),
            "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
+           "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
+           "context_tokens_per_s": r["tokens"] / w.kv_heads / (r["us_per_step"] * 1e-6),
            "roofline_attend": roofline_of(r, w.name), "layers_rotated": r["layers_rotated"],
            "read_between_visits_gb": round(r["read_between_visits"] / 1e9, 3), "chunk_blocks": r["plan"][0]}
     if scan_only:
@@ -692,7 +694,8 @@ def main():
                    "read_between_visits_gb": round(r["read_between_visits"] / 1e9, 3),
                    "chunk_blocks": r["plan"][0]},
         "effective_gbps": round(r["step_bytes"] / (r["us_per_step"] * 1e3), 1),
-        "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),
+        "kv_tokens_per_s": r["tokens"] / (r["us_per_step"] * 1e-6),  # KV token-heads (tokens x KV heads) per s
+        "context_tokens_per_s": r["tokens"] / w.kv_heads / (r["us_per_step"] * 1e-6),  # sum_b L_b per s
         "us_per_step_spread": r["replay_spread"],
         "attend_kernel_us": round(r["attend_us_mean"], 3),
         "decode_loop_us_per_step": round(r["loop_us_per_step"], 3),
