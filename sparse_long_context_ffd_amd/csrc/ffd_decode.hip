@@ -19,7 +19,10 @@
 // attends inside the kept blocks (the GQA union, its own kept blocks, or its
 // own tokens by the per-token criterion of Method 2), ART the run-time
 // termination of each chunk's refine stream (the ART page, "Attention Run-time
-// Termination", Method 2.2-2.4).
+// Termination", Method 2.2-2.4).  DBG compiles in the optional diagnostic
+// outputs (block maxima, keep flags, token masks, pseudo-maxima); the
+// in-grid union kernel is also built without them for calls that request
+// none, so that the common step carries none of their code.
 //
 // Scores are computed per 16-token tile with MFMA 16x16x32 f16, tokens on the
 // rows.  The B operand holds q with column n = 4*h + g carrying head h
@@ -137,9 +140,15 @@ struct AttendCfg {
 // estimates after the scan (so that the wait for the published words overlaps
 // the scan).  Without PMG the thresholds come from the separate launch's
 // partial maxima before the scan, which takes the decisions as it goes.
-template <int G, int SEL, bool ART, bool PMG>
+template <int G, int SEL, bool ART, bool PMG, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 : 2))) void attend_kernel(
     DecodeParams p) {
+  if constexpr (!DBG) {  // (launched only when every diagnostic pointer is null)
+    p.dbg_mt = nullptr;
+    p.dbg_bmax = nullptr;
+    p.dbg_keep = nullptr;
+    p.dbg_tmask = nullptr;
+  }
   constexpr int NT = AttendCfg<G>::NT, CBMAX = AttendCfg<G>::CBMAX;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, hc = col >> 2, gc = col & 3, ks = lane >> 4;
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // after the pseudo-max work-groups have published), the thresholds are
   // known before the scan and the blocks are decided as they are scanned.
   // Otherwise (usually at the start of the grid) the words still missing are
-  // loaded again before the scan and checked after it, where the thresholds
+  // loaded again during the scan and checked after it, where the thresholds
   // are first needed; words still missing then are polled a bounded number
   // of times, after which (or before the merge has initialised the sync
   // words, or under pm_local) the work-group computes the pseudo-max itself.
@@ -363,15 +372,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
     if (chunk == 0 && p.dbg_mt && tid < G) p.dbg_mt[(size_t)b * p.Hq + qh0 + tid] = pseudo_max(tid);
   };
   if (!PMG || pm_early) compute_thresholds();
-  const bool pm_had = pm_mine;  // (a second load of a missing word goes out after the scan)
-  if (pm_trusted && !pm_mine) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // A word still missing is loaded again inside the last scan batch: late
+  // enough that the pseudo-max work-groups have usually published it by then,
+  // early enough that it is back when the scan ends.
+  const bool pm_reload = pm_trusted && !pm_mine;
 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
   // sequence end (only in the last block) are set to -inf under tail_mask
-  auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint32_t (&zw)[4]) {
+  auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint32_t (&zw)[4], bool last) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
+      if (PMG && last && v == 1 && pm_reload) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int j = j0 + v;
       if (j < nbl) {
         const uint4 z4 = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[0], (int)zw[v]),
@@ -432,38 +444,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   int i0 = 0;
   for (; i0 + 2 < nbat; i0 += 2) {
     load_batch(4 * (i0 + 1), cwB, zwB);
-    scan_batch(4 * i0, cwA, zwA);
+    scan_batch(4 * i0, cwA, zwA, false);
     load_batch(4 * (i0 + 2), cwA, zwA);
-    scan_batch(4 * (i0 + 1), cwB, zwB);
+    scan_batch(4 * (i0 + 1), cwB, zwB, false);
   }
   if (i0 + 1 < nbat) {
     load_batch(4 * (i0 + 1), cwB, zwB);
-    scan_batch(4 * i0, cwA, zwA);
-    scan_batch(4 * (i0 + 1), cwB, zwB);
+    scan_batch(4 * i0, cwA, zwA, false);
+    scan_batch(4 * (i0 + 1), cwB, zwB, true);
   } else {
-    scan_batch(4 * i0, cwA, zwA);
+    scan_batch(4 * i0, cwA, zwA, true);
   }
 
   // ---- PMG: pseudo-maxima, thresholds and the reach flags after the scan ----
   if (PMG && !pm_early) {
     bool pm_fb = false;
     {
-      // a missing word is loaded once more now, while the load issued before
-      // the scan is checked; a stale first copy then waits only for this one
-      unsigned long long pw2 = pw;
-      if (pm_trusted && !pm_had) pw2 = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
-      if (!pm_mine) {
-        pw = pw2;
-        pm_mine = (uint32_t)(pw >> 32) == pm_want;
-      }
       // The thread's part goes to LDS before the vote, so that one barrier
       // publishes both; a value whose word is stale is never read (the
       // work-group then takes the fallback below, which rewrites what it reads).
       pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
       bool all = wg_all(pm_trusted && pm_mine, vote[1], wave, lane);
+      // words still missing: polled, the first time at once
       for (int s = 0; !all && pm_trusted && s < kPmSpin; ++s) {
-        __builtin_amdgcn_s_sleep(8);
+        if (s > 0) __builtin_amdgcn_s_sleep(8);
         if (!pm_mine) {
           pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           pm_mine = (uint32_t)(pw >> 32) == pm_want;
@@ -989,10 +994,10 @@ static void launch_merge(const DecodeParams& p, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int G, int SEL, bool ART, bool PMG>
+template <int G, int SEL, bool ART, bool PMG, bool DBG = true>
 static void launch_attend(const DecodeParams& p, hipStream_t s) {
   const dim3 grid = PMG ? dim3((unsigned)((p.npart + p.nchunk) * p.Hkv * p.B)) : dim3(p.nchunk, p.Hkv, p.B);
-  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG>), grid, dim3(256), AttendCfg<G>::lds_bytes(p.cb, p.dbg_bmax != nullptr), s,
+  hipLaunchKernelGGL((attend_kernel<G, SEL, ART, PMG, DBG>), grid, dim3(256), AttendCfg<G>::lds_bytes(p.cb, p.dbg_bmax != nullptr), s,
                      p);
 }
 template <int G>
@@ -1009,7 +1014,10 @@ static void launch_ffd_g(const DecodeParams& p, hipStream_t s) {
     }
   } else if (stages & 2) {
     if (p.ev_start) (void)hipEventRecord(p.ev_start, s);
-    if (p.pm_in_grid)  // (union selection without run-time termination only)
+    const bool dbg = p.dbg_mt || p.dbg_bmax || p.dbg_keep || p.dbg_tmask;
+    if (p.pm_in_grid && !dbg)  // (union selection without run-time termination only)
+      launch_attend<G, kSelectUnion, false, true, false>(p, s);
+    else if (p.pm_in_grid)
       launch_attend<G, kSelectUnion, false, true>(p, s);
     else if (p.art_patience > 0)  // run-time termination (union selection only)
       launch_attend<G, kSelectUnion, true, false>(p, s);
