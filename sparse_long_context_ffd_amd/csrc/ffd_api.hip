@@ -404,7 +404,6 @@ int decode_impl(const ffd_shape_t* shape, const void* q, const ffd_cache_t* cach
 
   ffd::DecodeParams p = {};
   p.select = selection;
-  p.interleaved = o.art_patience > 0 ? 0 : 1;  // a termination stream is a contiguous chunk
   p.art_patience = o.art_patience;
   p.art_tau = o.art_tau;
   p.art_phi = o.art_phi;

@@ -57,11 +57,11 @@ __global__ __launch_bounds__(256) void pseudomax_kernel(DecodeParams p) {
   __shared__ uint32_t qs[G * 64];
   typename QFrags<G>::Stage qst;
   QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
-  const int L = clamp_len(p, b);
+  const int L = clamp_len_uniform(p, b);
   SupportTile st;
   support_tile_load(p, part, head, L, wave, lane, st);
   QFrags<G>::stage_store(qst, tid, qs);
-  __syncthreads();
+  lds_barrier();  // q staged in LDS (the support tile loads stay in flight)
   typename QFrags<G>::Load ql;
   QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
@@ -102,11 +102,11 @@ __device__ void pm_group(const DecodeParams& p, int part, int hkv, int b, uint32
   typename QFrags<G>::Stage qst;
   QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
   const unsigned long long ep = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int L = clamp_len(p, b);
+  const int L = clamp_len_uniform(p, b);
   SupportTile st;
   support_tile_load(p, part, head, L, wave, lane, st);
   QFrags<G>::stage_store(qst, tid, qs);
-  __syncthreads();
+  lds_barrier();  // q staged in LDS (the support tile loads stay in flight)
   typename QFrags<G>::Load ql;
   QFrags<G>::load(qs, lane, ql);
   QFrags<G> qf;
@@ -191,6 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const int nbl_cap = blocks_below(p.nblk_cap);
   const size_t head = (size_t)b * p.Hkv + hkv;
   const int qh0 = hkv * G;
+  const int L = clamp_len_uniform(p, b);
   const TileOffsets to(wave, lane);
   // per-head buffer descriptors; lane offsets in VGPRs, block offsets in SGPRs
   const size_t hb = head * p.nblk_cap;  // first block of the head
@@ -199,7 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const __amdgpu_buffer_rsrc_t r_sz = make_rsrc(p.sz + hb * kSzBytes, nbc * kSzBytes);
 
   // ---- prologue: all loads issued together (q first: it is stored to LDS
-  // while the thumbnail batch is still in flight) ----
+  // and turned into MFMA fragments while the thumbnail batch is still in
+  // flight) ----
   typename QFrags<G>::Stage qst;
   QFrags<G>::stage_load(p.q + ((size_t)b * p.Hq + qh0) * kHeadDim, tid, qst);
   // Thumbnail batches: per lane 8 bytes of codes (the token's row of the A
@@ -225,9 +227,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   unsigned long long pw = 0, pm_magic = 0, pm_epoch = 0;  // in-grid word of (part tid/G, head tid%G), sync
   unsigned long long* const pm_word = p.pm_words + ((size_t)b * p.npart + tid / G) * p.Hq + qh0 + tid % G;
   if constexpr (PMG) {  // (the host keeps npart * G <= 256 here: one word per thread)
-    if (tid < n_pm) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pm_magic = __hip_atomic_load(p.pm_sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pm_epoch = __hip_atomic_load(p.pm_sync + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // device-coherent plain loads: as atomic loads they would hold the q
+    // barrier below until they land
+    const __amdgpu_buffer_rsrc_t r_pw = make_rsrc(p.pm_words + (size_t)b * p.npart * p.Hq, (uint32_t)(p.npart * p.Hq * 8));
+    {  // every thread loads (threads past n_pm repeat the last word), so that the load counters are exact
+      const int t = min(tid, n_pm - 1);
+      const uint2 w = buf_load_b64<kDeviceCoherent>(r_pw, (uint32_t)(((t / G) * p.Hq + qh0 + t % G) * 8), 0u);
+      pw = (unsigned long long)w.y << 32 | w.x;
+    }
+    const uint4 sy = buf_load_b128<kDeviceCoherent>(make_rsrc(p.pm_sync, 16), 0u, 0u);  // magic, epoch
+    pm_magic = (unsigned long long)sy.y << 32 | sy.x;
+    pm_epoch = (unsigned long long)sy.w << 32 | sy.z;
   } else {
     const float* pm = p.pmax + (size_t)b * p.npart * p.Hq + qh0;
     if (tid < n_pm) pm_t = pm[(size_t)(tid / G) * p.Hq + tid % G];
@@ -249,10 +259,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   CombineLds<G>& cl = *reinterpret_cast<CombineLds<G>*>(dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float));
   float* tmax = dyn + (AttendCfg<G>::est_bytes(cb) + sizeof(CombineLds<G>)) / sizeof(float);  // [cb][4*kWaves][G]
 
-  const int L = clamp_len(p, b);
   const int nblk = (L + 63) >> 6;
   const int nbl = blocks_below(nblk);
-  if (nbl <= 0) return;
+  if (nbl <= 0) {  // a chunk past the sequence end: empty partial (weight 0 in the merge)
+    if (tid < G) p.part_ml[((size_t)b * p.Hq + qh0 + tid) * p.nchunk + chunk] = make_float2(-INFINITY, 0.f);
+    return;
+  }
+  lds_barrier();  // q staged in LDS (the thumbnail batch stays in flight)
+  typename QFrags<G>::Load ql;
+  QFrags<G>::load(qs, lane, ql);
+  QFrags<G> qf;
+  qf.build(ql, lane);
   const bool dbg_bmax = p.dbg_bmax != nullptr;
   // Rows past the sequence end get estimate -inf only where it can matter:
   // with a local window the block holding the last token is always kept (and
@@ -277,13 +294,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   bool pm_mine = tid >= n_pm || (uint32_t)(pw >> 32) == pm_want;
   bool pm_early = false;
   if constexpr (PMG) {
-    // the thread's part goes to LDS with its vote; the vote's barrier also
-    // publishes q (a part whose word is stale is never read)
+    // the thread's part goes to LDS with its vote (a part whose word is stale
+    // is never read)
     pm_s[tid] = tid < n_pm ? __builtin_bit_cast(float, (uint32_t)pw) : -INFINITY;
     pm_early = wg_all(pm_trusted && pm_mine, vote[0], wave, lane);
   } else {
     pm_s[tid] = pm_t;
-    __syncthreads();  // q staged in LDS, and the partial maxima
+    __syncthreads();  // the partial maxima
   }
   // Refine loads of a block: residual, its scales, V.
   // lane's V^T span: channels 8*col..8*col+7 of token quad 4*wave+ks (64 bytes).
@@ -320,10 +337,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   constexpr bool kForcedFirst = !ART;
   RefineRegs X, Y;
   if (kForcedFirst && fmask) load_block(__builtin_ctzll(fmask), X);
-  typename QFrags<G>::Load ql;
-  QFrags<G>::load(qs, lane, ql);
-  QFrags<G> qf;
-  qf.build(ql, lane);
   int zsrc[kGroups];  // lanes holding the (scale, zero) pairs of this lane's token, groups 0..3
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) zsrc[g] = (col | (g << 4)) << 2;
@@ -536,7 +549,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   }
   if constexpr (SEL != kSelectHeadBlock)
     if (lane == 0) wkf[wave] = wk;
-  __syncthreads();
+  lds_barrier();
 
   // ---- block decisions (every wave derives the same mask) ----
   // forced blocks: [0, sink_end) and [local_beg, nblk)
@@ -798,9 +811,12 @@ __global__ __launch_bounds__(256) void dense_kernel(DecodeParams p) {
   }
   __shared__ float pw[kWaves][16 * PG];
   __shared__ CombineLds<G> cl;
-  const int L = clamp_len(p, b);
+  const int L = clamp_len_uniform(p, b);
   const int nblk = (L + 63) >> 6;
-  if (blk0 >= nblk) return;
+  if (blk0 >= nblk) {  // a chunk past the sequence end: empty partial (weight 0 in the merge)
+    if (tid < G) p.part_ml[((size_t)b * p.Hq + qh0 + tid) * p.nchunk + chunk] = make_float2(-INFINITY, 0.f);
+    return;
+  }
   const int nbl = min(p.cb, nblk - blk0);
   WaveSoftmax<G, 1> st;
   st.init();
@@ -876,10 +892,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
     ml_stride = G;
     o_stride = (size_t)G * kHeadDim;
   } else {
-    // chunks holding blocks of the sequence: the first ceil(nblk / cb) when
-    // chunks are contiguous (dense), every chunk below nblk when interleaved
-    const int nblk = (clamp_len(p, b) + 63) >> 6;
-    nch = p.interleaved ? min(p.nchunk, nblk) : (nblk + p.cb - 1) / p.cb;
+    // every chunk of the launch: each writes its (m, l), l = 0 when empty
+    // (no block of the sequence, or nothing kept), so the partials are read
+    // without waiting for the sequence length
+    nch = p.nchunk;
     ml = p.part_ml + row * p.nchunk;
     po = p.part_o + row * p.nchunk * kHeadDim + ch;
     ml_stride = 1;
@@ -948,11 +964,13 @@ __global__ __launch_bounds__(64) void merge64_kernel(DecodeParams p) {
     __hip_atomic_store(p.pm_sync, p.pm_magic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const size_t row = blockIdx.x >> 2;  // query head row; blockIdx.x & 3 = channel quarter
-  const int b = (int)(row / p.Hq), ch = 32 * (blockIdx.x & 3) + (lane & 31), half = lane >> 5;
-  const int nblk = (clamp_len(p, b) + 63) >> 6;
-  const int nch = p.interleaved ? min(p.nchunk, nblk) : (nblk + p.cb - 1) / p.cb;
-  // partial o of chunk c at byte c * 512 + 4 * channel; chunks past nch read
-  // as zero (bounds of the descriptor) and carry weight 0
+  const int ch = 32 * (blockIdx.x & 3) + (lane & 31), half = lane >> 5;
+  // Every chunk of the launch writes its (m, l), an empty chunk (no block of
+  // the sequence, or nothing kept) l = 0, so the partials are read without
+  // waiting for the sequence length; partial o of chunk c at byte
+  // c * 512 + 4 * channel, read as zero past the last chunk (bounds of the
+  // descriptor); a chunk of weight 0 contributes nothing.
+  const int nch = p.nchunk;
   const __amdgpu_buffer_rsrc_t r_o = make_rsrc(p.part_o + row * p.nchunk * kHeadDim, (uint32_t)nch * 512u);
   const float2 v = lane < nch ? p.part_ml[row * p.nchunk + lane] : make_float2(-INFINITY, 0.f);
   const uint32_t v_off = (uint32_t)ch * 4u + (uint32_t)half * 4u * 512u;  // + chunk (phase 4 * half)

@@ -107,6 +107,10 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 // 1 GiB).  Lines that several instructions read in turn must keep the default
 // policy: with the hint each of them fetches the line again.
 constexpr int kNonTemporal = 2;
+// kDeviceCoherent (the `sc1` bit) reads at device scope, past stale copies in
+// another XCD's L2: the policy an agent-scope atomic load is issued with, as a
+// plain load, so that a barrier ordering LDS only need not wait for it.
+constexpr int kDeviceCoherent = 16;
 // 16-byte global load with the non-temporal hint (same rule as above)
 __device__ inline uint4 load_b128_nt(const void* ptr) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -140,6 +144,15 @@ __device__ inline uint32_t opaque_vgpr(uint32_t k) {
 }
 __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { return (x & mask) | bits; }
 
+// Work-group barrier that orders LDS accesses only: global loads still in
+// flight stay in flight (__syncthreads also waits for every outstanding
+// vector memory access of the wave).  For hand-overs through LDS.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // True in every thread iff `pred` holds in every thread of a work-group of
 // four waves: one vote per wave in `vote` (4 ints in LDS, 16-byte aligned) and
 // one barrier.  Consecutive calls must alternate between two vote arrays (a
@@ -147,7 +160,7 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) { re
 __device__ inline bool wg_all(bool pred, int* vote, int wave, int lane) {
   const bool w = __builtin_amdgcn_ballot_w64(!pred) == 0;
   if (lane == 0) vote[wave] = w ? 1 : 0;
-  __syncthreads();
+  lds_barrier();
   const int4 v = *reinterpret_cast<const int4*>(vote);
   return (v.x & v.y & v.z & v.w) != 0;
 }

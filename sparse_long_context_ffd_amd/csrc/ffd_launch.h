@@ -46,7 +46,6 @@ struct DecodeParams {
   int select;              // kSelectUnion / kSelectHeadBlock / kSelectHeadToken
   int art_patience;        // run-time termination: stable steps before a chunk stops (0 = off)
   float art_tau, art_phi;  // ... thresholds on the probe's norm change and 1 - cosine
-  int interleaved;         // chunk c holds blocks c + j * nchunk (attend) instead of c * cb + j (dense)
   int pm_in_grid;          // 1: pseudo-max work-groups lead the attend grid (no separate launch)
   int pm_local;            // 1: every chunk computes the pseudo-max itself (tests the fallback)
   unsigned long long pm_magic;  // kPmMagic keyed to the word layout (written by the merge, checked by chunks)

@@ -18,6 +18,13 @@ __device__ inline int clamp_len(const DecodeParams& p, int b) {
   const int L = p.seq_lens[b];
   return L < 1 ? 1 : (L > p.L_cap ? p.L_cap : L);
 }
+// The same for a work-group-uniform b, read through the scalar cache (the
+// lengths are never written by a launch that reads them), so that the load
+// does not queue behind the vector loads issued with it.
+__device__ inline int clamp_len_uniform(const DecodeParams& p, int b) {
+  const int L = ((const __attribute__((address_space(4))) int*)p.seq_lens)[b];
+  return L < 1 ? 1 : (L > p.L_cap ? p.L_cap : L);
+}
 
 // quad (4 adjacent lanes) sum, result in every lane of the quad
 __device__ inline float quad_sum(float v) {
