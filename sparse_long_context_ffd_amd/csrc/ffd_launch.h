@@ -17,30 +17,14 @@ constexpr int kSelectHeadToken = 2;  // support tokens and tokens reaching the h
 constexpr unsigned long long kPmMagic = 0x4646442d706d6178ull;
 constexpr int kPmSpin = 4096;
 
+// Field order: the scalars and the pointers every attend work-group reads come
+// first, so that they share the first 64-byte lines of the kernel-argument
+// segment that a work-group's first scalar loads bring in (a field on a later
+// line costs one more scalar-cache round trip, on the critical path of a
+// short step); rarely used pointers and host-only fields come last.
 struct DecodeParams {
-  const uint16_t* q;       // [B][Hq][128] fp16
-  const uint8_t* codes;    // packed cache fields (layouts in include/ffd.h)
-  const uint8_t* sz;
-  const int8_t* res;
-  const uint8_t* rsc;
-  const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
-  const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]: token-quad tiled (FFD), natural (dense)
-  const int32_t* seq_lens; // [B]
-  float* pmax;             // [B][npart][Hq] partial pseudo-maxima (separate pseudo-max launch)
-  // Pseudo-max inside the attend launch: the first npart work-groups of each
-  // (batch, KV head) row publish their part's maxima as 64-bit words
-  // (epoch + 1) << 32 | fp32 bits; the merge advances the epoch once per step.
-  unsigned long long* pm_words;  // [B][npart][Hq]
-  unsigned long long* pm_sync;   // [0] kPmMagic once initialised, [1] epoch (low 32 bits)
-  float* part_o;           // [B][Hq][nchunk][128]
-  float2* part_ml;         // [B][Hq][nchunk] (m, l)
-  float* dbg_mt;           // optional [B][Hq]
-  float* dbg_bmax;         // optional [B][Hq][nblk_cap]
-  uint8_t* dbg_keep;       // optional [B][Hkv][nblk_cap]
-  uint8_t* dbg_tmask;      // optional [B][Hq][L_cap]: token attended by the head (kept blocks only)
-  uint16_t* out;           // [B][Hq][128] fp16
-  hipEvent_t ev_start;     // optional, recorded around the attend kernel
-  hipEvent_t ev_stop;
+  int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
+  float delta, sm_scale;
   int stages;              // bit 0: pseudo-max, bit 1: scan + refine, bit 2: merge (split path:
                            // bit 3 the scan kernel alone, bit 4 the refine kernel alone)
   int select;              // kSelectUnion / kSelectHeadBlock / kSelectHeadToken
@@ -48,16 +32,37 @@ struct DecodeParams {
   float art_tau, art_phi;  // ... thresholds on the probe's norm change and 1 - cosine
   int pm_in_grid;          // 1: pseudo-max work-groups lead the attend grid (no separate launch)
   int pm_local;            // 1: every chunk computes the pseudo-max itself (tests the fallback)
-  unsigned long long pm_magic;  // kPmMagic keyed to the word layout (written by the merge, checked by chunks)
   // split path (long caches): scan kernel -> keep bitmap words, refine kernel
   // over the compacted kept blocks -> per-unit partials [slot][G] (o, m, l)
   int split;               // 1: scan + refine kernels instead of the fused attend kernel
-  uint32_t* kmask;         // [B * Hkv][nword_cap] keep bitmap words (bit j: block 32 * word + j)
-  int* unit_start;         // [B * Hkv + 1] first refine unit of each (sequence, KV head)
   int nword_cap;           // ceil(nblk_cap / 32)
   int refine_groups;       // refine work-groups
-  int B, Hq, Hkv, L_cap, nblk_cap, nchunk, cb, npart, sink, local;
-  float delta, sm_scale;
+  unsigned long long pm_magic;  // kPmMagic keyed to the word layout (written by the merge, checked by chunks)
+  const uint16_t* q;       // [B][Hq][128] fp16
+  const uint8_t* codes;    // packed cache fields (layouts in include/ffd.h)
+  const uint8_t* sz;
+  const int8_t* res;
+  const uint8_t* rsc;
+  const uint16_t* v;       // fp16 V [B][Hkv][L_cap][128]: token-quad tiled (FFD), natural (dense)
+  const int32_t* seq_lens; // [B]
+  // Pseudo-max inside the attend launch: the first npart work-groups of each
+  // (batch, KV head) row publish their part's maxima as 64-bit words
+  // (epoch + 1) << 32 | fp32 bits; the merge advances the epoch once per step.
+  unsigned long long* pm_words;  // [B][npart][Hq]
+  unsigned long long* pm_sync;   // [0] kPmMagic once initialised, [1] epoch (low 32 bits)
+  float* part_o;           // [B][Hq][nchunk][128]
+  float2* part_ml;         // [B][Hq][nchunk] (m, l)
+  uint16_t* out;           // [B][Hq][128] fp16
+  const uint16_t* k;       // dense baseline: fp16 K [B][Hkv][L_cap][128]
+  float* pmax;             // [B][npart][Hq] partial pseudo-maxima (separate pseudo-max launch)
+  uint32_t* kmask;         // [B * Hkv][nword_cap] keep bitmap words (bit j: block 32 * word + j)
+  int* unit_start;         // [B * Hkv + 1] first refine unit of each (sequence, KV head)
+  float* dbg_mt;           // optional [B][Hq]
+  float* dbg_bmax;         // optional [B][Hq][nblk_cap]
+  uint8_t* dbg_keep;       // optional [B][Hkv][nblk_cap]
+  uint8_t* dbg_tmask;      // optional [B][Hq][L_cap]: token attended by the head (kept blocks only)
+  hipEvent_t ev_start;     // optional, recorded around the attend kernel (host only)
+  hipEvent_t ev_stop;
 };
 
 hipError_t launch_pack(const void* k, int B, int Hkv, int L_cap, int t_begin, int t_end, void* codes,
