@@ -124,7 +124,8 @@ template <int G>
 struct AttendCfg {
   static constexpr int NT = QFrags<G>::NT;
   static constexpr int CBMAX = (G <= 4) ? 32 : 24;
-  static constexpr size_t est_bytes(int cb) { return (size_t)cb * kWaves * G * 16 * sizeof(float); }
+  // (room for whole batches of 4 blocks: a last batch past the chunk's end is computed and dropped)
+  static constexpr size_t est_bytes(int cb) { return (size_t)((cb + 3) & ~3) * kWaves * G * 16 * sizeof(float); }
   static constexpr size_t tmax_bytes(int cb) { return (size_t)cb * 4 * kWaves * G * sizeof(float); }
   // the block-max diagnostic's area is allocated only when it is requested
   static constexpr size_t lds_bytes(int cb, bool bmax) {
@@ -226,13 +227,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   float pm_t = -INFINITY;
   unsigned long long pw = 0, pm_magic = 0, pm_epoch = 0;  // in-grid word of (part tid/G, head tid%G), sync
   unsigned long long* const pm_word = p.pm_words + ((size_t)b * p.npart + tid / G) * p.Hq + qh0 + tid % G;
+  // the same word as a device-coherent plain load (threads past n_pm read the last one)
+  const __amdgpu_buffer_rsrc_t r_pw = make_rsrc(p.pm_words + (size_t)b * p.npart * p.Hq, (uint32_t)(p.npart * p.Hq * 8));
+  const uint32_t pw_off = (uint32_t)(((min(tid, n_pm - 1) / G) * p.Hq + qh0 + min(tid, n_pm - 1) % G) * 8);
   if constexpr (PMG) {  // (the host keeps npart * G <= 256 here: one word per thread)
     // device-coherent plain loads: as atomic loads they would hold the q
     // barrier below until they land
-    const __amdgpu_buffer_rsrc_t r_pw = make_rsrc(p.pm_words + (size_t)b * p.npart * p.Hq, (uint32_t)(p.npart * p.Hq * 8));
     {  // every thread loads (threads past n_pm repeat the last word), so that the load counters are exact
-      const int t = min(tid, n_pm - 1);
-      const uint2 w = buf_load_b64<kDeviceCoherent>(r_pw, (uint32_t)(((t / G) * p.Hq + qh0 + t % G) * 8), 0u);
+      const uint2 w = buf_load_b64<kDeviceCoherent>(r_pw, pw_off, 0u);
       pw = (unsigned long long)w.y << 32 | w.x;
     }
     const uint4 sy = buf_load_b128<kDeviceCoherent>(make_rsrc(p.pm_sync, 16), 0u, 0u);  // magic, epoch
@@ -344,6 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   int n_pt = min(n_pm, (256 / G) * G) / G;  // parts held in pm_s
   float thr[NT];    // threshold of the lane column's head, in dot-product units
   float thr_t[NT];  // threshold of the lane's head in the transposed scan (row group ks)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) thr[nt] = thr_t[nt] = INFINITY;  // (until known)
   auto pseudo_max = [&](int h) {
     float m = -INFINITY;
     for (int pp = 0; pp < n_pt; ++pp) m = fmaxf(m, pm_s[pp * G + h]);
@@ -393,57 +397,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   // ---- phase A: estimate tile `wave` of every block of the chunk ----
   // estimates are kept as dot products (logit / sm_scale); rows past the
   // sequence end (only in the last block) are set to -inf under tail_mask
+  // A batch is straight-line code: blocks past the chunk's end (only in its
+  // last batch) are estimated from the clamped loads and dropped (the
+  // estimate array has room for them, and their reach bits are masked), so
+  // that the compiler interleaves the four blocks' LDS, MFMA and FMA
+  // latencies instead of running them one after another.
+  const bool decide_now = !PMG || pm_early;  // (work-group uniform)
+  const int row_lim = tail_mask ? L : INT_MAX;  // rows at or past it get estimate -inf
   auto scan_batch = [&](int j0, const uint2 (&cw)[4], const uint32_t (&zw)[4], bool last) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      if (PMG && last && v == 1 && pm_reload) pw = __hip_atomic_load(pm_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (PMG && last && v == 1) {  // every thread loads; the threads with a stale word take it
+        const uint2 w2 = buf_load_b64<kDeviceCoherent>(r_pw, pw_off, 0u);
+        pw = pm_reload ? ((unsigned long long)w2.y << 32 | w2.x) : pw;
+      }
       const int j = j0 + v;
-      if (j < nbl) {
-        const uint4 z4 = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[0], (int)zw[v]),
-                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[1], (int)zw[v]),
-                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[2], (int)zw[v]),
-                                    (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[3], (int)zw[v]));
-        float e[NT];
-        qf.estimate_t(cw[v], z4, e);
-        if (tail_mask && (blk_of(j) + 1) * 64 > L) {
-          const bool valid = blk_of(j) * 64 + 16 * wave + col < L;
+      const bool live = j < nbl;
+      const uint4 z4 = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[0], (int)zw[v]),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[1], (int)zw[v]),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[2], (int)zw[v]),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(zsrc[3], (int)zw[v]));
+      float e[NT];
+      qf.estimate_t(cw[v], z4, e);
+      const bool valid = blk_of(j) * 64 + 16 * wave + col < row_lim;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) e[nt] = valid ? e[nt] : -INFINITY;
-        }
-        // per-head block selection: bit h = head h reaches its threshold in
-        // this tile (lanes 16*ks .. 16*ks + 15 hold head 4*nt + ks); otherwise
-        // bit j of the wave's reach mask: some head of the group reaches it
-        // (without PMG; with it after the scan)
-        uint32_t hreach = 0;
-        bool reach = false;
+      for (int nt = 0; nt < NT; ++nt) e[nt] = valid ? e[nt] : -INFINITY;
+      // per-head block selection: bit h = head h reaches its threshold in
+      // this tile (lanes 16*ks .. 16*ks + 15 hold head 4*nt + ks); otherwise
+      // bit j of the wave's reach mask: some head of the group reaches it
+      // (without PMG; with it after the scan)
+      uint32_t hreach = 0;
+      bool reach = false;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (!PMG || pm_early) {
-            if constexpr (SEL == kSelectHeadBlock) {
-              const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
-              hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
-                         (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
-                        << (4 * nt);
-            } else {
-              reach = reach || (e[nt] >= thr_t[nt]);
-            }
-          }
-          const int h = 4 * nt + ks;
-          if (h < G) est[((j * kWaves + wave) * G + h) * 16 + col] = e[nt];
-          if (dbg_bmax) {
-            // block-max diagnostic: maximum over each 4-token quad of lanes
-            float qm = fmaxf(e[nt], dpp<kQuadXor1>(e[nt]));
-            qm = fmaxf(qm, dpp<kQuadXor2>(qm));
-            if (h < G && (col & 3) == 0) tmax[(j * 4 * kWaves + 4 * wave + (col >> 2)) * G + h] = qm;
-          }
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (SEL == kSelectHeadBlock) {
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(e[nt] >= thr_t[nt]);
+          hreach |= (((bal & 0xffffull) != 0) | (((bal >> 16) & 0xffffull) != 0) << 1 |
+                     (((bal >> 32) & 0xffffull) != 0) << 2 | (((bal >> 48) & 0xffffull) != 0) << 3)
+                    << (4 * nt);
+        } else {
+          reach |= e[nt] >= thr_t[nt];
         }
-        if (!PMG || pm_early) {
-          if constexpr (SEL == kSelectHeadBlock) {
-            if (lane == 0) kflag[wave][j] = (int)hreach;
-          } else {
-            wk |= __builtin_amdgcn_ballot_w64(reach) != 0 ? 1ull << j : 0ull;
-          }
+        const int h = 4 * nt + ks;
+        if (h < G) est[((j * kWaves + wave) * G + h) * 16 + col] = e[nt];
+        if (dbg_bmax && live) {
+          // block-max diagnostic: maximum over each 4-token quad of lanes
+          float qm = fmaxf(e[nt], dpp<kQuadXor1>(e[nt]));
+          qm = fmaxf(qm, dpp<kQuadXor2>(qm));
+          if (h < G && (col & 3) == 0) tmax[(j * 4 * kWaves + 4 * wave + (col >> 2)) * G + h] = qm;
         }
+      }
+      // (bitwise, not short-circuit, so that no branch splits the batch)
+      if constexpr (SEL == kSelectHeadBlock) {
+        if (decide_now & live & (lane == 0)) kflag[wave][j] = (int)hreach;
+      } else {
+        const bool any = __builtin_amdgcn_ballot_w64(reach) != 0;
+        wk |= (decide_now & live & any) ? 1ull << j : 0ull;
       }
     }
   };
