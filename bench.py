@@ -75,14 +75,16 @@ FLUSH_BYTES = 1 << 30         # the pre-replay copy: 1 GiB read + 1 GiB written
 # HBM bytes per launch of the fused kernel, from two rocprofv3 --pmc passes over
 # `bench.py --workload W --no-long --no-variants --no-cpu-baseline --steps 20 --warmup 5`
 # (FETCH_SIZE, then WRITE_SIZE: KiB per dispatch, median over the dispatches of
-# the attend kernel the step runs).  Both counters are scaled by what they read for the plain
+# the attend kernel the step runs, the launch with diagnostic outputs left out).  Both counters are scaled by what they read for the plain
 # 256 MiB device-to-device copy bench.py does first: FETCH_SIZE read 131088.6 KiB
 # for 262144 KiB moved (x2.0), WRITE_SIZE 262144 KiB (x1.0).  An entry counts only
 # while the kernel sources hash to the digest it was recorded with.
 FETCH_SCALE, WRITE_SCALE = 262144 / 131088.6, 1.0
 TRAFFIC_KIB = {
-    "llama8b_16k": {"sources": "af71b0047c026b29", "fetch": 10258.69, "write": 695.62},
-    "long_256k": {"sources": "af71b0047c026b29", "fetch": 133902.5, "write": 2464.59},
+    "llama8b_16k": {"sources": "dfbc5751e1d193e9", "fetch": 10225.75, "write": 695.5},
+    "long_256k": {"sources": "dfbc5751e1d193e9", "fetch": 133826.44, "write": 2465.94},
+    "qwen7b_b16_16k32k": {"sources": "dfbc5751e1d193e9", "fetch": 338044.16, "write": 5288.2},
+    "stress_b4_128k": {"sources": "dfbc5751e1d193e9", "fetch": 902841.72, "write": 4382.78},
 }
 REPLAYS = 10  # replays of the K-step graph behind the reported spread (the first is the timed one)
 METRIC = "decode-attn µs/step + effective HBM GB/s vs peak, 16K–256K ctx"
