@@ -11,7 +11,7 @@ import pytest
 from oracle import ffd_oracle as orc
 from synthetic import WORKLOADS, Workload, make_case
 from tests.gpu_helpers import (SM_SCALE, cache_to_host, check_head, dev, gpu_decode, gpu_dense, gpu_pack, say,
-                               shape_for, torch_mod)
+                               shape_for, torch_mod, ws_bytes)
 
 pytestmark = pytest.mark.gpu
 
@@ -448,3 +448,49 @@ def test_graph_replay_matches_eager_on_a_long_grid():
     pk = orc.quantize_k(c["k"][2, 5])
     check_head(orc, c["q"][2, 5 * w.group:6 * w.group], pk, c["v"][2, 5], int(c["seq_lens"][2]), 5.0, got, 2, 5,
                w.group, label="graph long b2 h5")
+
+
+@pytest.mark.parametrize("G,cap,lens", [(4, 4096, [1, 70, 4096]), (7, 2048, [5, 2048])])
+def test_stale_workspace_never_reaches_the_merge(G, cap, lens):
+    """Every chunk of a launch writes its (m, l) -- a chunk past its sequence's
+    end, or one that keeps nothing, with l = 0 -- so the merges read all of the
+    launch's partials without waiting for the sequence lengths.  Rows far
+    shorter than the capacity leave most chunks past their end.  With the
+    workspace filled beforehand (all of it: the pseudo-max then takes its
+    fallback; then all but the sync words: the in-grid hand-over) with bytes
+    that read as a live partial (0x3F: m = l = 0.75) or as NaN (0xFF), each
+    output must equal, bit for bit, the same call's on a zero-filled
+    workspace: the production union step, the two selection variants,
+    run-time termination and the dense baseline."""
+    torch = torch_mod()
+    import sparse_long_context_ffd_amd as ffd
+    B = len(lens)
+    w = Workload(f"stale_g{G}", B, 2 * G, 2, cap, None, len_range=(1, cap), needles=3)
+    c = make_case(w, 7)
+    shape = shape_for(w)
+    cache = gpu_pack(shape, dev(c["k"], torch), dev(c["v"], torch))
+    qd, kd, vd = dev(c["q"], torch), dev(c["k"], torch), dev(c["v"], torch)
+    ld = dev(np.array(lens, np.int32), torch)
+
+    def run(fill, sync_kept, select="union", art=None, dense=False):
+        n = ffd.workspace_bytes(shape) if dense else ws_bytes(shape, select, art)
+        ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, w.q_heads, 128), dtype=torch.float16, device="cuda")
+        call = (lambda: ffd.dense_decode_attn(shape, qd, kd, vd, ld, SM_SCALE, out, ws)) if dense else \
+            (lambda: ffd.decode_attn(shape, qd, cache, ld, 5.0, SM_SCALE, out, ws, select=select, art=art))
+        call()  # (initialises the sync words)
+        ws[256 if sync_kept else 0:].fill_(fill)
+        call()
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy()
+
+    for label, kw in [("union", {}), ("head_block", {"select": "head_block"}),
+                      ("head_token", {"select": "head_token"}), ("art", {"art": (0.05, 0.01, 1, 4)}),
+                      ("dense", {"dense": True})]:
+        for sync_kept in (False, True):
+            say(f"stale workspace G={G} lens={lens} {label} sync words kept={sync_kept}")
+            ref = run(0x00, sync_kept, **kw)
+            for fill in (0x3F, 0xFF):
+                got = run(fill, sync_kept, **kw)
+                assert np.isfinite(got).all(), f"{label}: non-finite output from a workspace of {fill:#x} bytes"
+                assert np.array_equal(got, ref), f"{label}: output depends on the workspace's {fill:#x} bytes"
