@@ -226,8 +226,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   const int n_pm = p.npart * G;
   float pm_t = -INFINITY;
   unsigned long long pw = 0, pm_magic = 0, pm_epoch = 0;  // in-grid word of (part tid/G, head tid%G), sync
+  // the word polled with agent-scope atomic loads after the scan, and read in
+  // the prologue and during the scan as a device-coherent plain load (threads
+  // past n_pm read the last one)
   unsigned long long* const pm_word = p.pm_words + ((size_t)b * p.npart + tid / G) * p.Hq + qh0 + tid % G;
-  // the same word as a device-coherent plain load (threads past n_pm read the last one)
   const __amdgpu_buffer_rsrc_t r_pw = make_rsrc(p.pm_words + (size_t)b * p.npart * p.Hq, (uint32_t)(p.npart * p.Hq * 8));
   const uint32_t pw_off = (uint32_t)(((min(tid, n_pm - 1) / G) * p.Hq + qh0 + min(tid, n_pm - 1) % G) * 8);
   if constexpr (PMG) {  // (the host keeps npart * G <= 256 here: one word per thread)
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 3 
   __shared__ float art_lds[ART ? 2 : 1][ART ? kWaves * (2 + kArtProbe) : 1];
   extern __shared__ __align__(16) float dyn[];
   const int cb = p.cb;
-  float* est = dyn;  // [cb][kWaves][G][16]
+  float* est = dyn;  // [cb rounded up to whole batches of 4][kWaves][G][16]
   CombineLds<G>& cl = *reinterpret_cast<CombineLds<G>*>(dyn + AttendCfg<G>::est_bytes(cb) / sizeof(float));
   float* tmax = dyn + (AttendCfg<G>::est_bytes(cb) + sizeof(CombineLds<G>)) / sizeof(float);  // [cb][4*kWaves][G]
 
